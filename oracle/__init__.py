@@ -1,0 +1,123 @@
+"""fp64 CPU oracle for packed block-diagonal attention (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package.  The product library never loads it; the two share no code.
+
+The arithmetic lives in ``pfa_oracle.c`` (plain C, fp64, two passes per row: exact
+row maximum first, then normaliser and weighted sum).  This module only builds and
+marshals:
+
+* ``varlen_fwd(q, k, v, cu_seqlens, scale, rows=None)`` -> ``(out, lse)``:
+  ``out`` is ``[T, H, dv]`` fp64 and ``lse`` is ``[H, T]`` fp64 (natural log), or
+  ``[n, H, dv]`` / ``[H, n]`` for a row sample ``rows``.
+* ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
+  probability matrix over all ``T`` tokens (zero off-segment).
+
+Inputs may be fp64 arrays or bf16 bit patterns (``uint16``), laid out ``[T, H, d]``
+as in the packed_attention listing of the Mage-Flow page (section on native-resolution
+sequence packing).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pfa_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ELEM_F64 = 0
+ELEM_BF16 = 1
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (fp64, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp"
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+               "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = ctypes.CDLL(_SO)
+        vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.pfa_oracle_fwd.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64, vp, vp]
+        lib.pfa_oracle_fwd.restype = i32
+        lib.pfa_oracle_probs.argtypes = [i32, vp, vp, vp, i32, i32, i32, f64, i64, i32, vp]
+        lib.pfa_oracle_probs.restype = i32
+        lib.pfa_oracle_num_threads.argtypes = []
+        lib.pfa_oracle_num_threads.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _kind(a: np.ndarray) -> int:
+    if a.dtype == np.float64:
+        return ELEM_F64
+    if a.dtype == np.uint16:
+        return ELEM_BF16
+    raise TypeError(f"oracle inputs must be float64 or uint16 (bf16 bits), got {a.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def varlen_fwd(q, k, v, cu_seqlens, scale: float, rows=None):
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    kind = _kind(q)
+    if _kind(k) != kind or _kind(v) != kind:
+        raise TypeError("q, k and v must share one element type")
+    if q.ndim != 3 or k.shape != q.shape or v.ndim != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("expected q, k [T, H, d] and v [T, H, dv]")
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, d = q.shape
+    dv = v.shape[2]
+    num_seqs = cu.shape[0] - 1
+    if num_seqs < 1 or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens must have >= 2 entries and end at T")
+    if rows is None:
+        n = T
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.shape[0]
+    out = np.empty((n, H, dv), dtype=np.float64)
+    lse = np.empty((H, n), dtype=np.float64)
+    rc = _load().pfa_oracle_fwd(kind, _ptr(q), _ptr(k), _ptr(v), _ptr(cu), num_seqs, H, d, dv,
+                                float(scale), _ptr(rows_arr) if rows_arr is not None else None,
+                                n, _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out, lse
+
+
+def probs(q, k, cu_seqlens, scale: float, i: int, h: int):
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    kind = _kind(q)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, d = q.shape
+    p = np.empty(T, dtype=np.float64)
+    rc = _load().pfa_oracle_probs(kind, _ptr(q), _ptr(k), _ptr(cu), cu.shape[0] - 1, H, d,
+                                  float(scale), int(i), int(h), _ptr(p))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return p
+
+
+def num_threads() -> int:
+    return int(_load().pfa_oracle_num_threads())

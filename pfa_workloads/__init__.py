@@ -1,0 +1,208 @@
+"""Seeded synthetic inputs for packed varlen attention (shared by tests, smoke and bench).
+
+This module holds no attention arithmetic.  It draws the inputs, rounds them to bf16
+and builds segment tables; the oracle and the HIP path both consume what it returns.
+
+Recipe (every workload): ``numpy.random.default_rng(seed)`` draws Q, then K, then V,
+each ``standard_normal((T, H, d), float32)``; any per-head scaling is applied next;
+values are then rounded to bf16 (round-to-nearest-even) and returned as uint16 bit
+patterns.  Segment lengths follow the patch counts of the Mage-Flow page (section on
+native-resolution sequence packing: 512x512 -> 1024 tokens, 1024x1024 -> 4096,
+768x432 -> 1296 at patch 16) and the [batch 8, heads 8, 4096, 64] shape of the
+GigaPath-Flash page, section 4.1.  No dataset or trained weights are involved.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+# ----------------------------------------------------------------------------- bf16
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round-to-nearest-even (finite inputs)."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+# ----------------------------------------------------------------------- workloads
+
+def _c3_lengths():
+    base = [4096] * 7 + [1296] * 5 + [1024] * 4
+    perm = np.random.default_rng(0).permutation(len(base))
+    return [base[i] for i in perm]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    lengths: tuple
+    heads: int
+    head_dim: int
+    description: str
+    per_head_qk_scale: bool = False
+
+
+CONFIGS = {
+    "C1": Config("C1", (256, 64), 4, 64,
+                 "2 images (256^2 and 128^2 at patch 16), seg [256,64], 4 heads, d 64"),
+    "C2": Config("C2", (4096,) * 8, 8, 64,
+                 "8 sequences of 4096 packed, 8 heads, d 64 (GigaPath-Flash 4.1 shape)"),
+    "C3": Config("C3", tuple(_c3_lengths()), 24, 128,
+                 "Mage-Flow mixed pack: 7x4096 + 5x1296 + 4x1024 (seed-0 permutation), "
+                 "39,248 tokens, 24 heads, d 128"),
+    "C4": Config("C4", (4096,) * 8, 24, 128,
+                 "8x4096 packed, 24 heads, d 128, Q and K of head h scaled by 0.5+1.5h/23",
+                 per_head_qk_scale=True),
+    "C5a": Config("C5a", (65536,), 16, 128, "one segment of 65536 tokens, 16 heads, d 128"),
+    "C5b": Config("C5b", (65536, 16384, 4096, 1296, 1), 16, 128,
+                  "5-segment pack [65536,16384,4096,1296,1], 16 heads, d 128"),
+}
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu
+
+
+def flops(lengths, heads: int, head_dim: int) -> float:
+    """Counted work 4 * sum(L^2) * H * d (QK^T and PV, 2 flops per multiply-add)."""
+    return 4.0 * float(sum(int(L) * int(L) for L in lengths)) * heads * head_dim
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    q: np.ndarray          # uint16 bf16 bits [T, H, d]
+    k: np.ndarray
+    v: np.ndarray
+    cu_seqlens: np.ndarray  # int32 [num_seqs + 1]
+    lengths: tuple
+    heads: int
+    head_dim: int
+    scale: float
+    max_seqlen: int
+    seed: int
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.lengths)
+
+    @property
+    def flops(self) -> float:
+        return flops(self.lengths, self.heads, self.head_dim)
+
+
+def make(lengths, heads: int, head_dim: int, seed: int = 0, name: str = "custom",
+         per_head_qk_scale: bool = False, scale: float | None = None) -> Workload:
+    lengths = tuple(int(L) for L in lengths)
+    T = int(sum(lengths))
+    rng = np.random.default_rng(seed)
+    shape = (T, heads, head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if per_head_qk_scale:
+        s = (0.5 + 1.5 * np.arange(heads, dtype=np.float64) / max(heads - 1, 1)).astype(np.float32)
+        q *= s[None, :, None]
+        k *= s[None, :, None]
+    return Workload(name=name, q=bf16_bits(q), k=bf16_bits(k), v=bf16_bits(v),
+                    cu_seqlens=cu_from_lengths(lengths), lengths=lengths, heads=heads,
+                    head_dim=head_dim,
+                    scale=float(scale) if scale is not None else 1.0 / math.sqrt(head_dim),
+                    max_seqlen=max(lengths) if lengths else 0, seed=seed)
+
+
+def generate(name: str, seed: int = 0) -> Workload:
+    c = CONFIGS[name]
+    return make(c.lengths, c.heads, c.head_dim, seed=seed, name=name,
+                per_head_qk_scale=c.per_head_qk_scale)
+
+
+def sample_rows(cu_seqlens, stride: int = 61, edge: int = 128, full_upto: int = 4096) -> np.ndarray:
+    """Deterministic row sample for configurations too large for the oracle in full.
+
+    Keeps rows r of segment [a, b) with (r - a) % stride == 0, rows within ``edge`` of
+    either segment end, and every row of segments no longer than ``full_upto``.  A prime
+    stride walks every residue of a power-of-two tile size.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    keep = []
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        r = np.arange(a, b)
+        if b - a <= full_upto:
+            keep.append(r)
+            continue
+        m = ((r - a) % stride == 0) | (r - a < edge) | (b - 1 - r < edge)
+        keep.append(r[m])
+    return np.concatenate(keep) if keep else np.zeros(0, dtype=np.int64)
+
+
+def random_lengths(rng: np.random.Generator, n: int, max_len: int, p_zero: float = 0.1,
+                   p_one: float = 0.1) -> list:
+    """Random segment lengths including the degenerate 0 and 1 cases."""
+    out = []
+    for _ in range(n):
+        u = rng.random()
+        if u < p_zero:
+            out.append(0)
+        elif u < p_zero + p_one:
+            out.append(1)
+        else:
+            out.append(int(rng.integers(2, max_len + 1)))
+    return out
+
+
+# ------------------------------------------------- SparseAttn worked-example inputs
+
+@dataclasses.dataclass
+class WorkedExample:
+    q: np.ndarray       # float64 [2 heads, n, d]; k is the same array
+    v: np.ndarray       # float64 [n, 3], shared by both heads
+    frame: np.ndarray   # frame index of each token (frame-major order)
+    pixel: np.ndarray   # position index within the frame
+    frames: int
+    positions: int
+
+
+def worked_example() -> WorkedExample:
+    """Inputs of the jefxiong.cn SparseAttn article's section-4 experiment.
+
+    4 frames of 4x4 = 16 positions, n = 64 tokens in frame-major order, d = 4 + 16 = 20.
+    Head 0 carries a signal of 6 on the one-hot of the token's frame, head 1 on the
+    one-hot of its position (offset by the 4 frame dimensions); Gaussian noise of
+    standard deviation 0.15 is added to both heads, drawn first from
+    ``default_rng(7)``; keys equal queries; the shared values, drawn next, are
+    N(0, 1) of shape (64, 3).
+    """
+    rng = np.random.default_rng(7)
+    frames, positions = 4, 16
+    n, d = frames * positions, frames + positions
+    frame = np.repeat(np.arange(frames), positions)
+    pixel = np.tile(np.arange(positions), frames)
+    q = np.zeros((2, n, d), dtype=np.float64)
+    q[0, np.arange(n), frame] = 6.0
+    q[1, np.arange(n), frames + pixel] = 6.0
+    q = q + rng.normal(0.0, 0.15, size=q.shape)
+    v = rng.normal(size=(n, 3))
+    return WorkedExample(q=q, v=v, frame=frame, pixel=pixel, frames=frames, positions=positions)

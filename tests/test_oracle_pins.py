@@ -1,0 +1,293 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows.  None compares the oracle with a retyped copy
+of its own formula: the pins are printed values (SparseAttn worked example), closed
+forms, a dense masked brute force, PyTorch's own attention routine, and invariants.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pfa_workloads as W
+from tests._brute import dense_block_diag
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "sparseattn_worked_example.json")
+
+
+def _printed_tol(s: str) -> float:
+    """Half a unit in the last printed digit (values on the page are rounded)."""
+    mant = s.lower().split("e")[0]
+    exp = int(s.lower().split("e")[1]) if "e" in s.lower() else 0
+    decimals = len(mant.split(".")[1]) if "." in mant else 0
+    return 0.5 * 10.0 ** (exp - decimals) * 1.001
+
+
+# ------------------------------------------------------------------ P-e worked example
+
+@pytest.fixture(scope="module")
+def worked():
+    ex = W.worked_example()
+    q = np.ascontiguousarray(ex.q.transpose(1, 0, 2))            # [64, 2, 20]
+    v = np.ascontiguousarray(np.repeat(ex.v[:, None, :], 2, 1))  # [64, 2, 3], shared by heads
+    scale = 1.0 / math.sqrt(q.shape[2])
+    n = q.shape[0]
+    full_o, full_l = oracle.varlen_fwd(q, q, v, [0, n], scale)
+    # same-frame mask == pack of the 4 frames (tokens are frame-major)
+    sf_o, sf_l = oracle.varlen_fwd(q, q, v, list(range(0, n + 1, ex.positions)), scale)
+    # same-position mask == pack of 16 groups of 4 after a stable sort by position
+    perm = np.argsort(ex.pixel, kind="stable")
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(n)
+    sp_o, sp_l = oracle.varlen_fwd(q[perm], q[perm], v[perm], list(range(0, n + 1, ex.frames)), scale)
+    sp_o, sp_l = sp_o[inv], sp_l[:, inv]
+    with open(GOLDEN) as f:
+        gold = json.load(f)["values"]
+    return dict(v=ex.v, full=(full_o, full_l), sf=(sf_o, sf_l), sp=(sp_o, sp_l), gold=gold)
+
+
+def _check(gold, key, value):
+    want = float(gold[key])
+    assert abs(value - want) <= _printed_tol(gold[key]), (key, value, want)
+
+
+@pytest.mark.parametrize("head,mask,prefix", [
+    (0, "sf", "spatial_head_same_frame"),
+    (0, "sp", "spatial_head_same_position"),
+    (1, "sf", "temporal_head_same_frame"),
+    (1, "sp", "temporal_head_same_position"),
+])
+def test_worked_example_retained_mass_and_mse(worked, head, mask, prefix):
+    """SparseAttn article, section 04 table: retained mass and MSE vs full attention."""
+    full_o, full_l = worked["full"]
+    o, l = worked[mask]
+    retained = np.exp(l[head] - full_l[head])          # z_i = sum_{j in S_i} p_ij (section 3.1)
+    mse = float(np.mean((o[:, head, :] - full_o[:, head, :]) ** 2))
+    _check(worked["gold"], prefix + "_retained_mass", float(retained.mean()))
+    _check(worked["gold"], prefix + "_mse", mse)
+
+
+def test_worked_example_row_error_and_bound(worked):
+    """SparseAttn article, sections 3.2 and 04: per-row error <= 2*alpha_i*M, printed maxima."""
+    full_o, full_l = worked["full"]
+    o, l = worked["sf"]
+    alpha = 1.0 - np.exp(l[0] - full_l[0])
+    err = np.linalg.norm(o[:, 0, :] - full_o[:, 0, :], axis=1)
+    M = np.linalg.norm(worked["v"], axis=1).max()
+    bound = 2.0 * np.maximum(alpha, 0.0) * M
+    assert np.all(err <= bound + 1e-12)
+    _check(worked["gold"], "spatial_head_same_frame_max_row_error", float(err.max()))
+    _check(worked["gold"], "spatial_head_same_frame_max_bound", float(bound.max()))
+
+
+def test_worked_example_full_mask_is_exact(worked):
+    """Section 04: the same inputs under the full mask reproduce full attention exactly."""
+    ex = W.worked_example()
+    q = np.ascontiguousarray(ex.q.transpose(1, 0, 2))
+    v = np.ascontiguousarray(np.repeat(ex.v[:, None, :], 2, 1))
+    o, l = oracle.varlen_fwd(q, q, v, [0, 64], 1.0 / math.sqrt(20))
+    assert np.array_equal(o, worked["full"][0]) and np.array_equal(l, worked["full"][1])
+
+
+# --------------------------------------------------------------------- P-f closed forms
+
+def test_single_token_segment_returns_its_value():
+    """L = 1: the only weight is 1, so O = v exactly and LSE = scale * q.k."""
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((5, 3, 8)); k = rng.standard_normal((5, 3, 8))
+    v = rng.standard_normal((5, 3, 4))
+    cu = [0, 2, 3, 5]                                   # token 2 is alone
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.7)
+    assert np.array_equal(o[2], v[2])
+    np.testing.assert_allclose(l[:, 2], 0.7 * np.sum(q[2] * k[2], axis=1), rtol=0, atol=1e-14)
+
+
+def test_zero_queries_give_segment_mean():
+    """q = 0 in a segment: uniform weights, O = mean of the segment's V, LSE = ln L."""
+    rng = np.random.default_rng(4)
+    T, H, d = 12, 2, 6
+    q = rng.standard_normal((T, H, d)); k = rng.standard_normal((T, H, d))
+    v = rng.standard_normal((T, H, 5))
+    q[4:11] = 0.0
+    cu = [0, 4, 11, 12]
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.3)
+    np.testing.assert_allclose(o[4:11], np.broadcast_to(v[4:11].mean(axis=0), (7, H, 5)), atol=1e-14)
+    np.testing.assert_allclose(l[:, 4:11], math.log(7), atol=1e-14)
+
+
+def test_constant_values_are_reproduced():
+    """V equal to c across a segment: any convex combination returns c."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((9, 1, 4)); k = rng.standard_normal((9, 1, 4))
+    v = rng.standard_normal((9, 1, 3)); v[3:9] = np.array([1.5, -2.0, 0.25])
+    o, _ = oracle.varlen_fwd(q, k, v, [0, 3, 9], 1.0)
+    np.testing.assert_allclose(o[3:9, 0], np.broadcast_to([1.5, -2.0, 0.25], (6, 3)), atol=1e-14)
+
+
+def test_two_key_counterexample():
+    """SparseAttn article, section 3.2: query 1, keys ln 99 and 0, values 0 and 100 give
+    probabilities 0.99/0.01 and output 1; keeping only the first key gives output 0."""
+    q = np.array([[[1.0]], [[1.0]]]); k = np.array([[[math.log(99.0)]], [[0.0]]])
+    v = np.array([[[0.0]], [[100.0]]])
+    o, l = oracle.varlen_fwd(q, k, v, [0, 2], 1.0)
+    np.testing.assert_allclose(o[:, 0, 0], [1.0, 1.0], atol=1e-12)
+    np.testing.assert_allclose(l[0], [math.log(100.0)] * 2, atol=1e-14)
+    p = oracle.probs(q, k, [0, 2], 1.0, 0, 0)
+    np.testing.assert_allclose(p, [0.99, 0.01], atol=1e-15)
+    o1, _ = oracle.varlen_fwd(q[:1], k[:1], v[:1], [0, 1], 1.0)      # retained set {key 0}
+    assert o1[0, 0, 0] == 0.0
+
+
+def test_large_logits_do_not_overflow():
+    """Logits near 1000: p = (3/4, 1/4) and LSE = 1000 + ln(4/3); a softmax that does not
+    subtract the row maximum overflows here."""
+    q = np.ones((2, 1, 1)); k = np.array([[[1000.0]], [[1000.0 - math.log(3.0)]]])
+    v = np.array([[[0.0]], [[4.0]]])
+    o, l = oracle.varlen_fwd(q, k, v, [0, 2], 1.0)
+    np.testing.assert_allclose(o[:, 0, 0], [1.0, 1.0], atol=1e-12)
+    np.testing.assert_allclose(l[0], 1000.0 + math.log(4.0 / 3.0), atol=1e-12)
+
+
+# -------------------------------------------------------- P-a brute force, P-h library
+
+def _random_case(seed, max_segs=7, max_len=40, H=3, d=16, dv=None, bf16=False):
+    rng = np.random.default_rng(seed)
+    lengths = W.random_lengths(rng, int(rng.integers(1, max_segs + 1)), max_len)
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    T = sum(lengths)
+    dv = dv or d
+    q = rng.standard_normal((T, H, d)); k = rng.standard_normal((T, H, d))
+    v = rng.standard_normal((T, H, dv))
+    if bf16:
+        q, k, v = W.bf16_bits(q), W.bf16_bits(k), W.bf16_bits(v)
+    return lengths, W.cu_from_lengths(lengths), q, k, v
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_matches_dense_brute_force(seed):
+    """Dense masked T x T softmax (GigaPath-Flash 4.1 naive form + SparseAttn -inf mask)."""
+    lengths, cu, q, k, v = _random_case(seed, dv=[16, 5, 16][seed % 3], bf16=seed % 2 == 1)
+    scale = 0.25 + 0.1 * seed
+    o, l = oracle.varlen_fwd(q, k, v, cu, scale)
+    qf, kf, vf = (W.bf16_to_f64(x) if x.dtype == np.uint16 else x for x in (q, k, v))
+    ob, lb = dense_block_diag(qf, kf, vf, cu, scale)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, lb, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_matches_torch_sdpa_fp64(seed):
+    """PyTorch's scaled_dot_product_attention (fp64, CPU, non-causal) run per segment,
+    and torch.logsumexp of the scaled scores for the LSE (GigaPath-Flash 4.3 names SDPA)."""
+    lengths, cu, q, k, v = _random_case(100 + seed, H=2, d=32)
+    scale = 1.0 / math.sqrt(32)
+    o, l = oracle.varlen_fwd(q, k, v, cu, scale)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        qs = torch.from_numpy(q[a:b]).permute(1, 0, 2)[None]
+        ks = torch.from_numpy(k[a:b]).permute(1, 0, 2)[None]
+        vs = torch.from_numpy(v[a:b]).permute(1, 0, 2)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, is_causal=False, scale=scale)
+        np.testing.assert_allclose(o[a:b], ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        lref = torch.logsumexp(scale * qs[0] @ ks[0].transpose(1, 2), dim=-1)
+        np.testing.assert_allclose(l[:, a:b], lref.numpy(), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------- invariants
+
+def test_probability_rows_sum_to_one_and_vanish_off_segment():
+    """Every row of the restricted softmax sums to 1 (SparseAttn section 3.1 renormalisation)
+    and assigns nothing outside the query's own segment (Mage-Flow: block-diagonal mask)."""
+    lengths, cu, q, k, v = _random_case(7, H=2, d=8)
+    T = cu[-1]
+    o, _ = oracle.varlen_fwd(q, k, v, cu, 0.5)
+    for i in range(0, T, 3):
+        s = int(np.searchsorted(cu[1:], i, side="right"))
+        for h in range(2):
+            p = oracle.probs(q, k, cu, 0.5, i, h)
+            assert abs(p.sum() - 1.0) < 1e-14
+            assert np.all(p[: cu[s]] == 0) and np.all(p[cu[s + 1]:] == 0)
+            np.testing.assert_allclose(p @ v[:, h, :], o[i, h], atol=1e-13)
+
+
+def test_pack_equals_each_segment_alone():
+    """A packed result equals every image run by itself (block-diagonal statement)."""
+    lengths, cu, q, k, v = _random_case(8, bf16=True)
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.4)
+    for s in range(len(lengths)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        os_, ls_ = oracle.varlen_fwd(q[a:b], k[a:b], v[a:b], [0, b - a], 0.4)
+        assert np.array_equal(o[a:b], os_) and np.array_equal(l[:, a:b], ls_)
+
+
+@pytest.mark.parametrize("poison", [np.nan, np.inf, 1e30])
+def test_other_segments_cannot_leak(poison):
+    """Poisoning every other segment leaves a segment's output bitwise unchanged
+    (LinearMem article: packed samples must not leak state; Mage-Flow block mask)."""
+    lengths, cu, q, k, v = _random_case(9)
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.5)
+    target = max(range(len(lengths)), key=lambda s: lengths[s])
+    a, b = int(cu[target]), int(cu[target + 1])
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    for arr in (q2, k2, v2):
+        arr[:a] = poison
+        arr[b:] = poison
+    o2, l2 = oracle.varlen_fwd(q2, k2, v2, cu, 0.5)
+    assert np.array_equal(o2[a:b], o[a:b]) and np.array_equal(l2[:, a:b], l[:, a:b])
+
+
+def test_permutation_equivariance():
+    """SparseAttn article, section 3.4: permuting tokens consistently (segment order, and
+    order inside a segment) permutes the outputs; fp64 differences stay at rounding."""
+    lengths, cu, q, k, v = _random_case(10, max_segs=5)
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.5)
+    rng = np.random.default_rng(11)
+    order = rng.permutation(len(lengths))
+    idx = []
+    for s in order:
+        a, b = int(cu[s]), int(cu[s + 1])
+        idx.extend(list(a + rng.permutation(b - a)))
+    idx = np.array(idx, dtype=np.int64)
+    cu2 = W.cu_from_lengths([lengths[s] for s in order])
+    o2, l2 = oracle.varlen_fwd(q[idx], k[idx], v[idx], cu2, 0.5)
+    np.testing.assert_allclose(o2, o[idx], rtol=0, atol=4e-15)
+    np.testing.assert_allclose(l2, l[:, idx], rtol=0, atol=4e-15)
+
+
+def test_deletion_mass_bound_between_pack_and_merged_sequence():
+    """SparseAttn article, section 3.2: ||O_pack - O_full|| <= 2 alpha_i max||v||, with
+    alpha_i = 1 - exp(LSE_pack - LSE_full) the probability mass the pack removes."""
+    lengths, cu, q, k, v = _random_case(12, H=2, d=4)
+    T = int(cu[-1])
+    op, lp = oracle.varlen_fwd(q, k, v, cu, 1.0)
+    of, lf = oracle.varlen_fwd(q, k, v, [0, T], 1.0)
+    for h in range(2):
+        alpha = np.maximum(1.0 - np.exp(lp[h] - lf[h]), 0.0)
+        M = np.linalg.norm(v[:, h, :], axis=1).max()
+        err = np.linalg.norm(op[:, h, :] - of[:, h, :], axis=1)
+        assert np.all(err <= 2 * alpha * M + 1e-12)
+
+
+def test_row_sample_matches_full_run():
+    lengths, cu, q, k, v = _random_case(13, bf16=True)
+    o, l = oracle.varlen_fwd(q, k, v, cu, 0.5)
+    rows = np.arange(0, int(cu[-1]), 2)
+    os_, ls_ = oracle.varlen_fwd(q, k, v, cu, 0.5, rows=rows)
+    assert np.array_equal(os_, o[rows]) and np.array_equal(ls_, l[:, rows])
+
+
+def test_rejects_malformed_tables():
+    q = np.zeros((4, 1, 2)); v = np.zeros((4, 1, 2))
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd(q, q, v, [0, 3, 2, 4], 1.0)      # decreasing
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd(q, q, v, [1, 4], 1.0)            # does not start at 0
