@@ -1,0 +1,108 @@
+/*
+ * pfa.h -- packed variable-length attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * Several images' patch tokens are concatenated into one sequence and an int32 prefix
+ * table cu_seqlens = [0, len0, len0+len1, ...] tells which rows belong to which image
+ * (Mage-Flow page, hankli.space, section "原生分辨率序列打包": the packed_attention
+ * listing, q/k/v shaped [total_tokens, num_heads, head_dim], cu_seqlens of shape (B+1,)
+ * int32, the varlen call with causal=False).  Tokens of different images never attend
+ * to each other: the attention matrix is block-diagonal (same page, the sentence after
+ * that listing).  The kernel tiles Q, K and V, keeps a running row maximum and
+ * normaliser, accumulates the output block by block and writes only the final result
+ * (lmnt.cn GigaPath-Flash page, section 3.2), which in exact arithmetic equals
+ *
+ *     O[i,h,:]  = sum_j exp(s_ij - M_i) v[j,h,:] / sum_j exp(s_ij - M_i)
+ *     LSE[h,i]  = M_i + ln sum_j exp(s_ij - M_i),   s_ij = scale * q[i,h,:].k[j,h,:]
+ *
+ * over the keys j of the query's own segment, M_i = max_j s_ij.
+ *
+ * Every function returns PFA_OK (0) or a negative pfa_status; nothing is thrown across
+ * this interface, and nothing is launched when an argument check fails.
+ */
+#ifndef PFA_H_
+#define PFA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PFA_API __attribute__((visibility("default")))
+
+typedef enum pfa_status {
+  PFA_OK = 0,
+  PFA_ERR_NULL = -1,          /* a required pointer is NULL                              */
+  PFA_ERR_NUM_SEQS = -2,      /* num_seqs < 1                                            */
+  PFA_ERR_HEADS = -3,         /* heads < 1                                               */
+  PFA_ERR_MAX_SEQLEN = -4,    /* max_seqlen < 1                                          */
+  PFA_ERR_HEAD_DIM = -5,      /* head_dim is not 64 or 128                               */
+  PFA_ERR_SCALE = -6,         /* scale is not finite and > 0                             */
+  PFA_ERR_ALIAS = -7,         /* out or lse is the same buffer as an input               */
+  PFA_ERR_CU_SEQLENS = -8,    /* host validator: malformed cu_seqlens table              */
+  PFA_ERR_DEVICE = -9,        /* no usable device, or a device query failed              */
+  PFA_ERR_LAUNCH = -10,       /* the kernel launch reported an error                     */
+  PFA_ERR_SIZE = -11          /* heads * head_dim or the table exceeds the int32 range   */
+} pfa_status;
+
+/*
+ * pfa_varlen_fwd -- packed, non-causal, block-diagonal attention forward.
+ *
+ * q, k, v     device pointers, bf16, contiguous [T, heads, head_dim]: row t, head h starts
+ *             at element (t*heads + h)*head_dim.  T = cu_seqlens[num_seqs] is known only on
+ *             the device; this call never reads the table on the host.  Read only.
+ * cu_seqlens  device pointer, int32 [num_seqs + 1]: segment s owns rows
+ *             [cu_seqlens[s], cu_seqlens[s+1]).  The same table serves queries and keys.
+ * num_seqs    number of segments (>= 1).  Zero-length segments are legal and do nothing.
+ * max_seqlen  an upper bound on every segment length (>= 1); sizes the launch only.
+ * heads       attention heads (>= 1); q, k and v all have this many (no grouped heads).
+ * head_dim    64 or 128.
+ * scale       factor on q.k, finite and > 0 (1/sqrt(head_dim) in the usual definition).
+ * out         device pointer, bf16 [T, heads, head_dim], written (round to nearest even).
+ * lse         device pointer, fp32 [heads, T], natural-log sum-exp of the scaled scores;
+ *             may be NULL when the caller does not need it.
+ * stream      HIP stream to enqueue on (0 = the null stream).  The call returns without
+ *             waiting; completion is the caller's to await.
+ *
+ * Ownership: the caller allocates and owns every buffer; out and lse must not overlap
+ * q, k, v or cu_seqlens.  The library allocates no device memory and keeps no state
+ * beyond a per-device cache of launch limits, so calls may run concurrently on
+ * different streams.
+ *
+ * Preconditions not checked here (checking them would need a device-to-host copy of the
+ * table): cu_seqlens[0] == 0, the table is non-decreasing, every length <= max_seqlen,
+ * and the buffers hold T rows.  Use pfa_check_cu_seqlens on a host copy to verify them.
+ * If they are violated the result is undefined, but the kernel still writes no row
+ * outside [0, cu_seqlens[num_seqs]).
+ *
+ * Results are deterministic: each output row and LSE entry is produced by exactly one
+ * workgroup in a fixed order, with no atomics.
+ */
+PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
+                           void* out, float* lse, hipStream_t stream);
+
+/*
+ * pfa_check_cu_seqlens -- host-side validator of a cu_seqlens table (no device calls).
+ *
+ * cu_host     host pointer to num_seqs + 1 int32 values.
+ * num_seqs    >= 1.
+ * max_seqlen  the bound that will be passed to pfa_varlen_fwd (>= 1).
+ * total_out   if not NULL, receives cu_host[num_seqs] (the packed token count T).
+ *
+ * Returns PFA_OK when cu_host[0] == 0, the table is non-decreasing and every segment
+ * length is <= max_seqlen; PFA_ERR_NULL, PFA_ERR_NUM_SEQS, PFA_ERR_MAX_SEQLEN or
+ * PFA_ERR_CU_SEQLENS otherwise.
+ */
+PFA_API int pfa_check_cu_seqlens(const int32_t* cu_host, int num_seqs, int max_seqlen,
+                                 int64_t* total_out);
+
+/* pfa_status_string -- static text for a status code (never NULL). */
+PFA_API const char* pfa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PFA_H_ */

@@ -1,0 +1,83 @@
+"""packed_varlen_flash_amd -- packed varlen attention forward on MI355X (gfx950).
+
+A thin Python face over the C ABI of ``libpfa.so`` (declared in ``include/pfa.h``).
+Every step of the computation runs in the library's HIP kernel; this module only checks
+tensor metadata, allocates outputs with PyTorch when the caller does not pass them, and
+hands raw pointers plus the current HIP stream to the library.  PyTorch is used for
+device memory and streams, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+
+__all__ = ["pfa_varlen_fwd", "pfa_check_cu_seqlens", "pfa_status_string", "PfaError",
+           "LIB_PATH"]
+
+LIB_PATH = _lib.LIB_PATH
+
+
+class PfaError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"pfa status {status}: {pfa_status_string(status)}")
+
+
+def pfa_status_string(status: int) -> str:
+    return _lib.load().pfa_status_string(int(status)).decode()
+
+
+def pfa_check_cu_seqlens(cu_host, max_seqlen: int) -> int:
+    """Validate a host copy of cu_seqlens; return T or raise PfaError."""
+    cu = np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    total = ctypes.c_int64(0)
+    rc = _lib.load().pfa_check_cu_seqlens(cu.ctypes.data_as(ctypes.c_void_p), cu.shape[0] - 1,
+                                          int(max_seqlen), ctypes.byref(total))
+    if rc != 0:
+        raise PfaError(rc)
+    return int(total.value)
+
+
+def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None,
+                   out=None, lse=None, want_lse: bool = True, stream=None):
+    """Packed block-diagonal attention forward.
+
+    q, k, v: bf16 CUDA tensors [T, H, d] (d = 64 or 128), contiguous.
+    cu_seqlens: int32 CUDA tensor [num_seqs + 1].  max_seqlen: bound on segment lengths.
+    Returns (out [T, H, d] bf16, lse [H, T] fp32 or None), enqueued on ``stream``
+    (default: PyTorch's current stream).
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor [T, H, d]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+    T, H, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_fwd(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, int(max_seqlen), H, d,
+        float(scale), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+        ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse

@@ -21,10 +21,19 @@ import numpy as np
 # ----------------------------------------------------------------------------- bf16
 
 def bf16_bits(x) -> np.ndarray:
-    """float32 -> bf16 bit patterns, round-to-nearest-even (finite inputs)."""
+    """float32 -> bf16 bit patterns, round-to-nearest-even.
+
+    Finite inputs only (the largest finite pattern plus the rounding increment still fits
+    in 32 bits); NaN and infinity patterns are passed through by truncation."""
     f = np.ascontiguousarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    finite = np.isfinite(f)
+    r = (u >> 16) & 1
+    r += u
+    r += np.uint32(0x7FFF)
+    r >>= 16
+    if not finite.all():
+        r[~finite] = u[~finite] >> 16
     return r.astype(np.uint16)
 
 

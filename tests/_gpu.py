@@ -1,0 +1,64 @@
+"""Helpers for GPU parity tests: upload seeded inputs, run the HIP path, compare."""
+import sys
+
+import numpy as np
+
+import pfa_workloads as W
+
+# Bars for bf16 inputs against the fp64 oracle: max |err| and relative RMS of the output,
+# max |err| of the LSE.
+MAX_ABS = 1e-2
+REL_RMS = 4e-3
+LSE_ABS = 1e-3
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def from_dev_bf16(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def upload(wl):
+    import torch
+    return (to_dev(wl.q), to_dev(wl.k), to_dev(wl.v),
+            torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to("cuda"))
+
+
+def run(wl, label="", want_lse=True, dev=None, stream=None):
+    """Run pfa_varlen_fwd on a Workload; returns (out bits [T,H,d] uint16, lse [H,T] f32)."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd
+    say(f"[gpu] pfa_varlen_fwd {label or wl.name}: segs={len(wl.lengths)} T={wl.total_tokens} "
+        f"H={wl.heads} d={wl.head_dim} max_seqlen={wl.max_seqlen}")
+    q, k, v, cu = dev if dev is not None else upload(wl)
+    out, lse = pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, want_lse=want_lse, stream=stream)
+    torch.cuda.synchronize()
+    return from_dev_bf16(out), (lse.cpu().numpy() if lse is not None else None)
+
+
+def compare(out_bits, lse, o_ref, l_ref):
+    o = W.bf16_to_f64(out_bits)
+    diff = o - o_ref
+    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    denom = float(np.sqrt(np.sum(o_ref * o_ref)))
+    rel_rms = float(np.sqrt(np.sum(diff * diff)) / denom) if denom > 0 else 0.0
+    lse_abs = float(np.abs(lse.astype(np.float64) - l_ref).max()) if lse is not None and lse.size else 0.0
+    return dict(max_abs=max_abs, rel_rms=rel_rms, lse_abs=lse_abs,
+                n_big=int(np.sum(np.abs(o_ref) >= 4.0)))
+
+
+def assert_parity(m, label=""):
+    say(f"[parity] {label}: max|err|={m['max_abs']:.3e} relRMS={m['rel_rms']:.3e} "
+        f"LSE={m['lse_abs']:.3e} (|O_ref|>=4: {m['n_big']})")
+    assert m["max_abs"] <= MAX_ABS, m
+    assert m["rel_rms"] <= REL_RMS, m
+    assert m["lse_abs"] <= LSE_ABS, m
