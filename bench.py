@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark: packed varlen attention forward on one MI355X.
+
+One step is one call of pfa_varlen_fwd over the whole packed batch (every segment, every
+head: tile scheduling, QK^T, masking, online softmax, PV, epilogue), with the inputs
+already resident in HBM.  The default workload is the Mage-Flow mixed pack (16 images,
+7x4096 + 5x1296 + 4x1024 tokens, 24 heads, head_dim 128).
+
+Prints one JSON line with the throughput (TFLOP/s = 4 * sum(L^2) * H * d / step time), a
+roofline object for the attention kernel (HIP events over the timed region, on the stream
+the kernel is launched on) and the fp64 oracle timed on the host's cores on a bounded
+row sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C3] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import pfa_workloads as W  # noqa: E402
+
+METRIC = "attention TFLOP/s (4·ΣL_i²·H·d) and % of bf16 MFMA peak, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0            # MI355X dense bf16 MFMA (published)
+KERNEL_SRC = os.path.join(ROOT, "packed_varlen_flash_amd", "csrc", "pfa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pfa_fwd_C3.json")
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(config: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken
+    on the kernel source as it is now; otherwise None."""
+    if config != "C3" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_sha256") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def describe(wl) -> str:
+    c = W.CONFIGS.get(wl.name)
+    return f"{wl.name}: {c.description}" if c else wl.name
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n,
+                      "bytes_written_per_copy": n, "copies": 3}))
+
+
+def cpu_baseline(wl, out_bits, lse, budget_s: float):
+    """Time the fp64 oracle on a bounded row sample of the same workload and compare the
+    GPU output on those rows."""
+    import oracle
+    rng = np.random.default_rng(1234)
+    T = wl.total_tokens
+    lengths = np.diff(wl.cu_seqlens)
+    seg_of = np.searchsorted(wl.cu_seqlens[1:], np.arange(T), side="right")
+    # a pilot of 24 rows sizes the sample to ~budget_s seconds of oracle work
+    pilot = np.sort(rng.choice(T, size=min(24, T), replace=False))
+    t0 = time.perf_counter()
+    oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale, rows=pilot)
+    per_row = (time.perf_counter() - t0) / len(pilot)
+    n = int(max(24, min(T, budget_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(T, size=n, replace=False))
+    t0 = time.perf_counter()
+    o_ref, l_ref = oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale, rows=rows)
+    dt = time.perf_counter() - t0
+    flop = 4.0 * float(lengths[seg_of[rows]].astype(np.float64).sum()) * wl.heads * wl.head_dim
+    o = W.bf16_to_f64(out_bits[rows])
+    diff = o - o_ref
+    parity = {"rows": int(n), "max_abs_err": float(np.abs(diff).max()),
+              "rel_rms": float(np.sqrt((diff * diff).sum() / (o_ref * o_ref).sum())),
+              "lse_max_abs_err": float(np.abs(lse[:, rows].astype(np.float64) - l_ref).max())}
+    base = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} uniformly drawn query rows of {wl.name} (all heads, each row against "
+                      f"its whole segment), {flop / 1e9:.1f} GFLOP of fp64 work in {dt:.1f} s"}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention of independent (segment, head) units needs no exchange; "
+              "sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    from packed_varlen_flash_amd import pfa_varlen_fwd
+
+    wl = W.generate(args.config, seed=args.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.heads, wl.total_tokens), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    flop = wl.flops
+    ms_per_step = wall * 1e3 / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (kernel_ms * 1e-3) / 1e12
+    traffic = measured_traffic(args.config)
+
+    out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    lse_h = lse.cpu().numpy()
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        cpu, parity = cpu_baseline(wl, out_bits, lse_h, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V; no dataset or weights)",
+        "config": {
+            "workload": describe(wl),
+            "segments": list(wl.lengths),
+            "total_tokens": wl.total_tokens,
+            "heads": wl.heads,
+            "head_dim": wl.head_dim,
+            "causal": False,
+            "flop_per_step": flop,
+            "seed": args.seed,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(kernel_ms, 5),
+        },
+        "cpu_baseline": cpu,
+        "parity_on_sample": parity,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
