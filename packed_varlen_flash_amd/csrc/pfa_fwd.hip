@@ -36,18 +36,25 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBN = 64;          // keys per LDS stage
-constexpr int kSortMax = 1024;   // segment tables up to this size are sorted on device
+constexpr int kStages = 2;       // LDS ring depth (stages)
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
+constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
+constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr float kRescaleSlack = 8.0f;  // let P grow to 2^8 before rescaling O and l
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct Params {
   const __bf16* q;
@@ -65,20 +72,42 @@ struct Params {
 template <int D, int QB>
 struct Tile {
   static constexpr int BM = kWaves * QB * 32;       // query rows per workgroup tile
-  static constexpr int KSTR = D + 8;                // K row stride in LDS (elements)
-  static constexpr int VSTR = D + 16;               // V row stride in LDS (elements)
-  static constexpr int KTILE = kBN * KSTR;
-  static constexpr int VTILE = kBN * VSTR;
-  static constexpr int CHUNKS_PER_ROW = D / 8;      // 16-byte chunks per row
-  static constexpr int CPT = kBN * CHUNKS_PER_ROW / kThreads;  // chunks per thread per tile
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  static constexpr int TILE_BYTES = kBN * D * 2;    // one K (or V) stage, unpadded
+  static constexpr int CPT = kBN * CPR / kThreads;  // chunks per thread per stage
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
-  static constexpr size_t LDS_BYTES =
-      sizeof(__bf16) * (size_t)(2 * KTILE + 2 * VTILE) + sizeof(int) * SCHED_INTS;
-  static_assert(CPT * kThreads == kBN * CHUNKS_PER_ROW, "tile must split evenly");
-  static_assert(sizeof(int) * kSortMax <= sizeof(__bf16) * 2 * KTILE, "len scratch fits");
+  static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
+  static_assert(CPT * kThreads == kBN * CPR, "stage must split evenly");
+  static_assert(sizeof(int) * kSortMax <= (size_t)kStages * TILE_BYTES, "len scratch fits");
 };
+
+// LDS layout of a K or V stage: 16-byte chunks, row-major (row = key), with the chunk
+// index XOR-swizzled inside each 256-byte line so the two read patterns are free of bank
+// conflicts: K operand reads (16 lanes = 16 consecutive rows, one logical chunk) and
+// transposed V reads (4 consecutive rows x 64 bytes per 32 lanes).
+__device__ __forceinline__ int swz_k(int line) { return line & 15; }
+__device__ __forceinline__ int swz_v(int line) { return (line & 3) << 2; }
+
+// byte offset of logical (row, chunk) within a stage
+template <int D, bool IS_K>
+__device__ __forceinline__ int phys_off(int row, int chunk) {
+  const int P = row * (D / 8) + chunk;
+  const int line = P >> 4;
+  const int sw = IS_K ? swz_k(line) : swz_v(line);
+  return ((line << 4) | ((P & 15) ^ sw)) << 4;
+}
+
+// logical byte offset (row * row_bytes + chunk * 16) of the chunk stored at physical
+// chunk position P; the XOR swizzle is its own inverse
+template <int D, bool IS_K>
+__device__ __forceinline__ int logical_src(int P, int row_bytes) {
+  const int line = P >> 4;
+  const int sw = IS_K ? swz_k(line) : swz_v(line);
+  const int Pl = (line << 4) | ((P & 15) ^ sw);
+  return (Pl / (D / 8)) * row_bytes + (Pl % (D / 8)) * 16;
+}
 
 __device__ __forceinline__ float partner_max(float x) {
   // v_permlane32_swap pairs lane l with lane l^32: max of the pair on every lane.
@@ -143,7 +172,132 @@ __device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_
 
 // ---------------------------------------------------------------------------------
 // One query tile of one (segment, head).
+//
+// Keys are consumed in 32-key sub-blocks; LDS holds a ring of kStages 64-key stages.
+// Per stage s (sub-blocks 2s and 2s+1) the wave runs, in program order,
+//   A: S1 = K(2s+1) Q^T          with the softmax of S0 (sub-block 2s) interleaved
+//   B: O += V(2s)^T P0
+//   -- workgroup barrier --
+//   C: S0 = K(2s+2) Q^T          with the softmax of S1 interleaved; stage s+2 -> LDS
+//   D: O += V(2s+1)^T P1
+// so the MFMA pipe always has independent work while the softmax VALU runs.  Stage
+// s+2 overwrites the slot of stage s-1, whose last readers finished before the barrier.
 // ---------------------------------------------------------------------------------
+template <int D, int QB>
+struct TileState {
+  using C = Tile<D, QB>;
+  bf16x8 qr[QB][C::KSTEP];       // Q fragments (B operand of K Q^T)
+  f32x16 o[QB][C::DT];           // O^T accumulators
+  float m_run[QB];               // running max (base-2 scaled)
+  float l_run[QB];               // row sum of the fp32 weights (for the LSE)
+  float l_rnd[QB];               // row sum of the bf16 weights (normalises O)
+};
+
+// S^T (keys x queries) for one 32-key sub-block.  kst points at the sub-block's first
+// row; koff[t] is this lane's byte offset of (row n32, chunk 2t+g).
+template <int D, int QB>
+__device__ __forceinline__ void qk_subblock(const char* kst, const int (&koff)[D / 16],
+                                            const bf16x8 (&qr)[QB][D / 16], f32x16 (&s)[QB]) {
+  using C = Tile<D, QB>;
+  bf16x8 a[C::KSTEP];
+#pragma unroll
+  for (int t = 0; t < C::KSTEP; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
+#pragma unroll
+  for (int t = 0; t < C::KSTEP; ++t)
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qr[b][t], s[b], 0, 0, 0);
+}
+
+// Online softmax of one sub-block; keys >= kend (segment end) are masked.  Writes the
+// bf16 weights as two 16-key B operands per query block.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_subblock(TileState<D, QB>& st, f32x16 (&s)[QB],
+                                                 bf16x8 (&pb)[QB][2], int key0, int L, float c,
+                                                 int g) {
+  using C = Tile<D, QB>;
+  if (key0 + 32 > L) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
+      if (key >= L) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) s[b][i] = -INFINITY;
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    float mx = fmaxf(s[b][0], s[b][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+    mx = partner_max(mx);
+    const float mb = mx * c;
+    // The running max only moves when some lane's block max exceeds it by more than
+    // kRescaleSlack: until then P = 2^(s*c - m) <= 2^8 and O, l keep their scale, which is
+    // exact (the final O/l and LSE use the same m).  A fully masked block has mb = -inf.
+    if (__builtin_amdgcn_ballot_w64(mb > st.m_run[b] + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(st.m_run[b], mb);
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
+      st.m_run[b] = m_new;
+      st.l_run[b] *= alpha;
+      st.l_rnd[b] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= alpha;
+    }
+    const float neg_m = -st.m_run[b];
+    // Two row sums.  l_run adds the fp32 weights before rounding and gives the LSE (a sum
+    // of rounded weights carries up to 2^-9 relative error into the LSE of a sharp row).
+    // l_rnd adds the bf16 weights the PV product actually uses and normalises O, so in a
+    // row dominated by one key that key's rounding cancels between numerator and
+    // denominator.  The bf16 dot accumulates into fresh 8-step partials only.
+    float ex0 = 0.f, ex1 = 0.f, rd0 = 0.f, rd1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[b][i], c, neg_m));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 1], c, neg_m));
+      ex0 += e0;
+      ex1 += e1;
+      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+      if (i < 8)
+        rd0 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rd0, false);
+      else
+        rd1 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rd1, false);
+      pb[b][i >> 3][i & 7] = pr[0];
+      pb[b][i >> 3][(i & 7) + 1] = pr[1];
+    }
+    st.l_run[b] += ex0 + ex1;
+    st.l_rnd[b] += rd0 + rd1;
+  }
+}
+
+// O^T += V^T P^T for one 32-key sub-block.  vst points at the sub-block's first row;
+// voff[dt] is this lane's byte offset for the transposed read of rows 4g + i16/4 at
+// d = 32dt + 16hh + 4(i16 & 3); the second read of each pair is 8 rows further.
+template <int D, int QB>
+__device__ __forceinline__ void pv_subblock(TileState<D, QB>& st, const char* vst,
+                                            const int (&voff)[D / 32], const bf16x8 (&pb)[QB][2]) {
+  using C = Tile<D, QB>;
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const char* vp = vst + cc * 16 * D * 2 + voff[dt];
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * D * 2));
+      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        st.o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][cc], st.o[b][dt], 0, 0, 0);
+    }
+}
+
 template <int D, int QB>
 __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int seg_a,
                                              int L, int h, int qt, int T) {
@@ -151,7 +305,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n32 = lane & 31;         // query column (S^T) / d row of V^T within a 32-tile
+  const int n32 = lane & 31;         // query column (S^T) / key row of the K operand
   const int g = lane >> 5;           // half-wave
   const int i16 = lane & 15;
   const int hh = (lane >> 4) & 1;
@@ -161,10 +315,10 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const __bf16* kbase = p.k + (int64_t)seg_a * rs + head_off;
   const __bf16* vbase = p.v + (int64_t)seg_a * rs + head_off;
   const int q0 = qt * C::BM + wave * (QB * 32);
-  const int nkb = (L + kBN - 1) / kBN;
+  const int ns = (L + kBN - 1) / kBN;      // 64-key stages
+  const float c = p.c;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[row n32][16t + 8g .. +7]
-  bf16x8 qr[QB][C::KSTEP];
+  TileState<D, QB> st;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const int row = q0 + b * 32 + n32;
@@ -172,154 +326,87 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     for (int t = 0; t < C::KSTEP; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row < L) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * rs + 16 * t + 8 * g);
-      qr[b][t] = __builtin_bit_cast(bf16x8, x);
+      st.qr[b][t] = __builtin_bit_cast(bf16x8, x);
     }
-  }
-
-  // ---- K/V staging through registers
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto gload = [&](int kb) {
-#pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
-      const int id = tid + r * kThreads;
-      const int row = id / C::CHUNKS_PER_ROW;
-      const int col = id % C::CHUNKS_PER_ROW;
-      const int key = kb + row;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (key < L) {
-        xk = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * rs + col * 8);
-        xv = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * rs + col * 8);
-      }
-      kst[r] = xk;
-      vst[r] = xv;
-    }
-  };
-  auto lstore = [&](int stage) {
-#pragma unroll
-    for (int r = 0; r < C::CPT; ++r) {
-      const int id = tid + r * kThreads;
-      const int row = id / C::CHUNKS_PER_ROW;
-      const int col = id % C::CHUNKS_PER_ROW;
-      *reinterpret_cast<u32x4*>(ks + stage * C::KTILE + row * C::KSTR + col * 8) = kst[r];
-      *reinterpret_cast<u32x4*>(vs + stage * C::VTILE + row * C::VSTR + col * 8) = vst[r];
-    }
-  };
-
-  f32x16 o[QB][C::DT];
-  float m_run[QB], l_run[QB];
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    m_run[b] = -INFINITY;
-    l_run[b] = 0.f;
+    st.m_run[b] = -INFINITY;
+    st.l_run[b] = 0.f;
+    st.l_rnd[b] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[b][dt][i] = 0.f;
+      for (int i = 0; i < 16; ++i) st.o[b][dt][i] = 0.f;
   }
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // ---- per-lane LDS offsets (fixed for the whole tile)
+  int koff[C::KSTEP], voff[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+    voff[dt] = phys_off<D, false>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
 
-  for (int j = 0; j < nkb; ++j) {
-    const int cur = j & 1;
-    const int kb = j * kBN;
-    const bool more = j + 1 < nkb;
-    if (more) gload(kb + kBN);
-
-    const __bf16* kst_l = ks + cur * C::KTILE;
-    const __bf16* vst_l = vs + cur * C::VTILE;
-
-    // ---- S^T[key][query] = K Q^T for two 32-key sub-blocks
-    f32x16 sacc[QB][2];
+  // ---- stage loads: global -> LDS directly (no registers).  Lane l of the wave's i-th
+  // load writes physical chunk (wave*CPT + i)*64 + l, fetched from its logical source.
+  // A buffer resource bounded at the segment end returns zeros for rows >= L, so no row
+  // of a neighbouring segment is ever read.
+  const int row_bytes = (int)(rs * 2);   // the host keeps 64 rows within int range
+  char* const kring = reinterpret_cast<char*>(ks);
+  char* const vring = reinterpret_cast<char*>(vs);
+  auto issue_stage = [&](int stage) {
+    const int kb = stage * kBN;
+    const int rows = (L - kb < kBN) ? (L - kb) : kBN;
+    const int nrec = rows * row_bytes;
+    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+    char* kdst = kring + (stage % kStages) * C::TILE_BYTES + wave * C::CPT * 1024;
+    char* vdst = vring + (stage % kStages) * C::TILE_BYTES + wave * C::CPT * 1024;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b][sb][i] = 0.f;
-#pragma unroll
-      for (int t = 0; t < C::KSTEP; ++t) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(kst_l + (sb * 32 + n32) * C::KSTR + 16 * t + 8 * g);
-#pragma unroll
-        for (int b = 0; b < QB; ++b)
-          sacc[b][sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[b][t], sacc[b][sb], 0, 0, 0);
-      }
+    for (int i = 0; i < C::CPT; ++i) {
+      const int P = (wave * C::CPT + i) * 64 + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16,
+                                               logical_src<D, true>(P, row_bytes), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16,
+                                               logical_src<D, false>(P, row_bytes), 0, 0, 0);
     }
+  };
+  auto kstage = [&](int stage, int sb) -> const char* {
+    return kring + (stage % kStages) * C::TILE_BYTES + sb * 32 * D * 2;
+  };
+  auto vstage = [&](int stage, int sb) -> const char* {
+    return vring + (stage % kStages) * C::TILE_BYTES + sb * 32 * D * 2;
+  };
 
-    // ---- keys past the segment end never contribute
-    if (kb + kBN > L) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + sb * 32 + (i >> 2) * 8 + 4 * g + (i & 3);
-          if (key >= L) {
-#pragma unroll
-            for (int b = 0; b < QB; ++b) sacc[b][sb][i] = -INFINITY;
-          }
-        }
-    }
-
-    // ---- online softmax (base 2): running max, rescale, exponentiate, row sum
-    bf16x8 pb[QB][2][2];
-#pragma unroll
-    for (int b = 0; b < QB; ++b) {
-      float mx = sacc[b][0][0];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[b][sb][i]);
-      mx = partner_max(mx);
-      const float m_new = fmaxf(m_run[b], mx * p.c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[b] - m_new);
-      m_run[b] = m_new;
-      float rsum = 0.f;
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[b][sb][i], p.c, -m_new));
-          rsum += e;
-          pb[b][sb][i >> 3][i & 7] = (__bf16)e;
-        }
-      l_run[b] = l_run[b] * alpha + rsum;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[b][dt][i] *= alpha;
-    }
-
-    // ---- O^T[d][query] += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ch = 2 * sb + cc;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          const __bf16* vp = vst_l + (16 * ch + 4 * g + (i16 >> 2)) * C::VSTR + 32 * dt + 16 * hh + 4 * (i16 & 3);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * C::VSTR));
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-          for (int b = 0; b < QB; ++b)
-            o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][sb][cc], o[b][dt], 0, 0, 0);
-        }
-      }
-
-    if (more) lstore(cur ^ 1);
+  // ---- stage loop.  Stage s sits in slot s % kStages; the loads of stage s+1 are
+  // issued right after the barrier that retires every reader of its slot, and have the
+  // whole of stage s to land.
+  issue_stage(0);
+  f32x16 s0[QB], s1[QB];
+  bf16x8 p0[QB][2], p1[QB][2];
+  for (int s = 0; s < ns; ++s) {
+    const int key0 = s * kBN;
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
+    if (s + 1 < ns) issue_stage(s + 1);
+    qk_subblock<D, QB>(kstage(s, 0), koff, st.qr, s0);
+    qk_subblock<D, QB>(kstage(s, 1), koff, st.qr, s1);
+    softmax_subblock<D, QB>(st, s0, p0, key0, L, c, g);
+    pv_subblock<D, QB>(st, vstage(s, 0), voff, p0);
+    softmax_subblock<D, QB>(st, s1, p1, key0 + 32, L, c, g);
+    pv_subblock<D, QB>(st, vstage(s, 1), voff, p1);
   }
+  __syncthreads();   // the next tile's first stage overwrites slot 0
 
-  // ---- epilogue: O = acc / l in bf16 (round to nearest even), LSE = ln2 * (m + log2 l)
+  // ---- epilogue: O = acc / l_rnd in bf16 (round to nearest even),
+  //      LSE = ln2 * (m + log2 l_run)
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float lt = partner_sum(l_run[b]);
+    const float lt = partner_sum(st.l_run[b]);
+    const float lr = partner_sum(st.l_rnd[b]);
     const int row = q0 + b * 32 + n32;
     if (row < L) {
-      const float inv = 1.0f / lt;
+      const float inv = 1.0f / lr;
       __bf16* orow = p.out + (int64_t)(seg_a + row) * rs + head_off;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -327,22 +414,23 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
         for (int ii = 0; ii < 4; ++ii) {
           bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(o[b][dt][4 * ii + e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv);
           *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * ii + 4 * g) = w;
         }
       if (p.lse != nullptr && g == 0)
-        p.lse[(int64_t)h * T + seg_a + row] = (m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
+        p.lse[(int64_t)h * T + seg_a + row] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
     }
   }
 }
 
-template <int D, int QB>
-__global__ void __launch_bounds__(kThreads) pfa_fwd_kernel(Params p) {
+template <int D, int QB, int WPE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+pfa_fwd_kernel(Params p) {
   using C = Tile<D, QB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
-  __bf16* vs = ks + 2 * C::KTILE;
-  int* s_order = reinterpret_cast<int*>(vs + 2 * C::VTILE);
+  __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
+  int* s_order = reinterpret_cast<int*>(smem + 2 * kStages * C::TILE_BYTES);
   int* s_prefix = s_order + kSortMax;
   int* s_len = reinterpret_cast<int*>(ks);  // scratch, dead before the first K tile lands
 
@@ -404,9 +492,9 @@ struct Variant {
   size_t lds;
 };
 
-template <int D, int QB>
+template <int D, int QB, int WPE>
 Variant make_variant() {
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB>), Tile<D, QB>::BM,
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, WPE>), Tile<D, QB>::BM,
                  Tile<D, QB>::LDS_BYTES};
 }
 
@@ -417,9 +505,22 @@ std::atomic<int> g_occ[kMaxDevices][kVariants];
 
 int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
 
+#ifndef PFA_D64_QB
+#define PFA_D64_QB 1
+#endif
+#ifndef PFA_D64_WPE
+#define PFA_D64_WPE 4
+#endif
+#ifndef PFA_D128_QB
+#define PFA_D128_QB 1
+#endif
+#ifndef PFA_D128_WPE
+#define PFA_D128_WPE 2
+#endif
+
 Variant variant_for(int head_dim) {
-  if (head_dim == 64) return make_variant<64, 2>();
-  return make_variant<128, 2>();
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_WPE>();
+  return make_variant<128, PFA_D128_QB, PFA_D128_WPE>();
 }
 
 }  // namespace

@@ -6,7 +6,7 @@ import numpy as np
 import pfa_workloads as W
 
 # Bars for bf16 inputs against the fp64 oracle: max |err| and relative RMS of the output,
-# max |err| of the LSE.
+# max |err| of the LSE (see the rounding note at compare()).
 MAX_ABS = 1e-2
 REL_RMS = 4e-3
 LSE_ABS = 1e-3
@@ -45,20 +45,38 @@ def run(wl, label="", want_lse=True, dev=None, stream=None):
     return from_dev_bf16(out), (lse.cpu().numpy() if lse is not None else None)
 
 
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), np.finfo(np.float32).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 8)
+
+
+# The 1e-2 bar leaves 1e-2 - 2^-7 for the kernel's own error at |O| in [2, 4), where bf16
+# rounding of the output alone can take 2^-7.  At |O| >= 4 rounding alone can exceed the
+# bar, so there the bound is that element's own rounding step plus the same allowance.
+KERNEL_ALLOWANCE = MAX_ABS - 2.0 ** -7
+
+
 def compare(out_bits, lse, o_ref, l_ref):
     o = W.bf16_to_f64(out_bits)
     diff = o - o_ref
-    max_abs = float(np.abs(diff).max()) if diff.size else 0.0
+    ad = np.abs(diff)
+    big = np.abs(o_ref) >= 4.0
+    max_abs = float(ad.max()) if diff.size else 0.0
+    max_abs_small = float(ad[~big].max()) if np.any(~big) else 0.0
+    excess_big = float((ad[big] - bf16_half_ulp(o_ref[big])).max()) if np.any(big) else -1.0
     denom = float(np.sqrt(np.sum(o_ref * o_ref)))
     rel_rms = float(np.sqrt(np.sum(diff * diff)) / denom) if denom > 0 else 0.0
     lse_abs = float(np.abs(lse.astype(np.float64) - l_ref).max()) if lse is not None and lse.size else 0.0
-    return dict(max_abs=max_abs, rel_rms=rel_rms, lse_abs=lse_abs,
-                n_big=int(np.sum(np.abs(o_ref) >= 4.0)))
+    return dict(max_abs=max_abs, max_abs_small=max_abs_small, excess_big=excess_big,
+                rel_rms=rel_rms, lse_abs=lse_abs, n_big=int(big.sum()))
 
 
 def assert_parity(m, label=""):
-    say(f"[parity] {label}: max|err|={m['max_abs']:.3e} relRMS={m['rel_rms']:.3e} "
-        f"LSE={m['lse_abs']:.3e} (|O_ref|>=4: {m['n_big']})")
-    assert m["max_abs"] <= MAX_ABS, m
+    say(f"[parity] {label}: max|err|={m['max_abs']:.3e} (|O_ref|<4: {m['max_abs_small']:.3e}; "
+        f"{m['n_big']} elements >=4, worst excess over rounding {m['excess_big']:.3e}) "
+        f"relRMS={m['rel_rms']:.3e} LSE={m['lse_abs']:.3e}")
+    assert m["max_abs_small"] <= MAX_ABS, m
+    assert m["excess_big"] <= KERNEL_ALLOWANCE, m
     assert m["rel_rms"] <= REL_RMS, m
     assert m["lse_abs"] <= LSE_ABS, m
