@@ -51,7 +51,12 @@ constexpr int kStages = 2;       // LDS ring depth (stages)
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
 constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
 constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
-constexpr float kRescaleSlack = 8.0f;  // let P grow to 2^8 before rescaling O and l
+// How far (base 2) a block max may exceed the running max before O and l are rescaled.
+// 0 keeps the reference equal to the exact running max, so the largest weight of a row is
+// exactly 1 and carries no bf16 rounding; a positive slack saves rescales (about 5% on
+// 4096-token segments) but leaves that weight rounded, which on sharp softmax rows pushes
+// the worst output error past 1e-2 of the exact result.
+constexpr float kRescaleSlack = 0.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -193,32 +198,70 @@ struct TileState {
   float l_rnd[QB];               // row sum of the bf16 weights (normalises O)
 };
 
-// S^T (keys x queries) for one 32-key sub-block.  kst points at the sub-block's first
-// row; koff[t] is this lane's byte offset of (row n32, chunk 2t+g).
-template <int D, int QB>
-__device__ __forceinline__ void qk_subblock(const char* kst, const int (&koff)[D / 16],
-                                            const bf16x8 (&qr)[QB][D / 16], f32x16 (&s)[QB]) {
-  using C = Tile<D, QB>;
-  bf16x8 a[C::KSTEP];
+// K operand fragments of one 32-key sub-block: kst points at the sub-block's first row;
+// koff[t] is this lane's byte offset of (row n32, chunk 2t+g).
+template <int D>
+__device__ __forceinline__ void k_operands(const char* kst, const int (&koff)[D / 16],
+                                           bf16x8 (&a)[D / 16]) {
 #pragma unroll
-  for (int t = 0; t < C::KSTEP; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
+  for (int t = 0; t < D / 16; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
+}
+
+// S^T (keys x queries) = K Q^T for one sub-block.
+template <int D, int QB>
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&a)[D / 16], const bf16x8 (&qr)[QB][D / 16],
+                                        f32x16 (&s)[QB]) {
 #pragma unroll
   for (int b = 0; b < QB; ++b)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
 #pragma unroll
-  for (int t = 0; t < C::KSTEP; ++t)
+  for (int t = 0; t < D / 16; ++t)
 #pragma unroll
     for (int b = 0; b < QB; ++b)
       s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qr[b][t], s[b], 0, 0, 0);
 }
 
-// Online softmax of one sub-block; keys >= kend (segment end) are masked.  Writes the
-// bf16 weights as two 16-key B operands per query block.
+// V^T operand fragments of one sub-block: vst points at its first row; voff[dt] is this
+// lane's byte offset for the transposed read of rows 4g + i16/4 at d = 32dt + 16hh +
+// 4(i16 & 3); the second read of each pair is 8 rows further.
+template <int D>
+__device__ __forceinline__ void v_operands(const char* vst, const int (&voff)[D / 32],
+                                           bf16x8 (&va)[2][D / 32]) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const char* vp = vst + cc * 16 * D * 2 + voff[dt];
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * D * 2));
+      va[cc][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
+// O^T += V^T P^T for one sub-block, 16 keys per MFMA.
 template <int D, int QB>
-__device__ __forceinline__ void softmax_subblock(TileState<D, QB>& st, f32x16 (&s)[QB],
-                                                 bf16x8 (&pb)[QB][2], int key0, int L, float c,
-                                                 int g) {
+__device__ __forceinline__ void pv_mfma(TileState<D, QB>& st, const bf16x8 (&va)[2][D / 32],
+                                        const bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        st.o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][dt], pb[b][cc], st.o[b][dt], 0, 0, 0);
+}
+
+// Online softmax, first half: mask keys past the segment end, take the block max and move
+// the running max when it is exceeded by more than kRescaleSlack.  Until then
+// P = 2^(s*c - m) <= 2^slack and O, l keep their scale, which is exact: the final O/l and
+// LSE use the same m.  A fully masked block has max -inf.  The row sums are rescaled at once;
+// O is rescaled here only when no weights computed against the old max are still waiting
+// to be added (DEFER_O false).  Otherwise the factor is returned in alpha (1 when the max
+// did not move) and the caller applies it after those weights have been accumulated.
+template <int D, int QB, bool DEFER_O>
+__device__ __forceinline__ bool softmax_head(TileState<D, QB>& st, f32x16 (&s)[QB], int key0,
+                                             int L, float c, int g, float (&alpha)[QB]) {
   using C = Tile<D, QB>;
   if (key0 + 32 > L) {
 #pragma unroll
@@ -230,33 +273,46 @@ __device__ __forceinline__ void softmax_subblock(TileState<D, QB>& st, f32x16 (&
       }
     }
   }
+  bool moved = false;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
+    alpha[b] = 1.f;
     float mx = fmaxf(s[b][0], s[b][1]);
 #pragma unroll
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
     mx = partner_max(mx);
     const float mb = mx * c;
-    // The running max only moves when some lane's block max exceeds it by more than
-    // kRescaleSlack: until then P = 2^(s*c - m) <= 2^8 and O, l keep their scale, which is
-    // exact (the final O/l and LSE use the same m).  A fully masked block has mb = -inf.
     if (__builtin_amdgcn_ballot_w64(mb > st.m_run[b] + kRescaleSlack) != 0) {
       const float m_new = fmaxf(st.m_run[b], mb);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
+      const float a = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
       st.m_run[b] = m_new;
-      st.l_run[b] *= alpha;
-      st.l_rnd[b] *= alpha;
+      st.l_run[b] *= a;
+      st.l_rnd[b] *= a;
+      alpha[b] = a;
+      moved = true;
+      if (!DEFER_O) {
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+        for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= alpha;
+          for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= a;
+      }
     }
+  }
+  return moved;
+}
+
+// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and the
+// two row sums.  l_run adds the fp32 weights before rounding and gives the LSE (a sum of
+// rounded weights carries up to 2^-9 relative error into the LSE of a sharp row).  l_rnd
+// adds the bf16 weights the PV product actually uses and normalises O, so in a row
+// dominated by one key that key's rounding cancels between numerator and denominator.
+// The bf16 dot accumulates into fresh 8-step partials only.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
+                                             bf16x8 (&pb)[QB][2], float c) {
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
     const float neg_m = -st.m_run[b];
-    // Two row sums.  l_run adds the fp32 weights before rounding and gives the LSE (a sum
-    // of rounded weights carries up to 2^-9 relative error into the LSE of a sharp row).
-    // l_rnd adds the bf16 weights the PV product actually uses and normalises O, so in a
-    // row dominated by one key that key's rounding cancels between numerator and
-    // denominator.  The bf16 dot accumulates into fresh 8-step partials only.
     float ex0 = 0.f, ex1 = 0.f, rd0 = 0.f, rd1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
@@ -277,25 +333,78 @@ __device__ __forceinline__ void softmax_subblock(TileState<D, QB>& st, f32x16 (&
   }
 }
 
-// O^T += V^T P^T for one 32-key sub-block.  vst points at the sub-block's first row;
-// voff[dt] is this lane's byte offset for the transposed read of rows 4g + i16/4 at
-// d = 32dt + 16hh + 4(i16 & 3); the second read of each pair is 8 rows further.
+// Keeps the bf16 weights and row sums of a softmax body where they are computed: without
+// it the compiler sinks them past the next branch, next to their use, which separates
+// them from the MFMAs they are meant to run beside.  Emits no instruction.
 template <int D, int QB>
-__device__ __forceinline__ void pv_subblock(TileState<D, QB>& st, const char* vst,
-                                            const int (&voff)[D / 32], const bf16x8 (&pb)[QB][2]) {
-  using C = Tile<D, QB>;
+__device__ __forceinline__ void pin_softmax(TileState<D, QB>& st, bf16x8 (&pb)[QB][2]) {
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+  for (int b = 0; b < QB; ++b) {
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const char* vp = vst + cc * 16 * D * 2 + voff[dt];
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * D * 2));
-      const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-        st.o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[b][cc], st.o[b][dt], 0, 0, 0);
+    for (int cc = 0; cc < 2; ++cc) {
+      u32x4 w = __builtin_bit_cast(u32x4, pb[b][cc]);
+      asm volatile("" : "+v"(w));
+      pb[b][cc] = __builtin_bit_cast(bf16x8, w);
     }
+    asm volatile("" : "+v"(st.l_run[b]), "+v"(st.l_rnd[b]));
+  }
+}
+
+// Interleave n MFMAs with the VALU work around them, `valu` VALU instructions after each.
+template <int N, int VALU>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  }
+}
+
+// One 64-key stage: issue the next stage's loads into its slot, then QK, softmax and PV
+// on the current slot.  The four LDS pointers are restrict-qualified: the next slot and
+// the current slot never overlap, which lets the compiler keep the current slot's reads
+// from waiting on the next slot's loads.  The straight-line half of each sub-block's
+// softmax shares a basic block with the MFMAs of the neighbouring sub-block (QK of the
+// next, PV of the previous), so the MFMA pipe and the VALU work side by side.
+template <int D, int QB, typename IssueFn>
+__device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restrict__ knext,
+                                           char* __restrict__ vnext, const char* __restrict__ kcur,
+                                           const char* __restrict__ vcur, bool issue,
+                                           const IssueFn& issue_fn, int s, int L,
+                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
+                                           float c, int g) {
+  constexpr int NQK = QB * D / 16;   // MFMAs of one sub-block's QK (and of its PV)
+  if (issue) issue_fn(knext, vnext, s + 1);
+  const int key0 = s * kBN;
+  f32x16 s0[QB], s1[QB];
+  bf16x8 p0[QB][2], p1[QB][2];
+  bf16x8 ka[D / 16], kb[D / 16];
+  bf16x8 va[2][D / 32];
+  float alpha[QB];
+  k_operands<D>(kcur, koff, ka);
+  qk_mfma<D, QB>(ka, st.qr, s0);
+  k_operands<D>(kcur + 32 * D * 2, koff, kb);
+  softmax_head<D, QB, false>(st, s0, key0, L, c, g, alpha);
+  qk_mfma<D, QB>(kb, st.qr, s1);
+  softmax_body<D, QB>(st, s0, p0, c);
+  interleave_mfma_valu<NQK, 8 * 16 / NQK>();
+  pin_softmax<D, QB>(st, p0);
+  v_operands<D>(vcur, voff, va);
+  // P0 was computed against the max before this head: O's rescale waits until P0 V is in
+  const bool moved = softmax_head<D, QB, true>(st, s1, key0 + 32, L, c, g, alpha);
+  pv_mfma<D, QB>(st, va, p0);
+  softmax_body<D, QB>(st, s1, p1, c);
+  interleave_mfma_valu<NQK, 8 * 16 / NQK>();
+  if (moved) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= alpha[b];
+  }
+  v_operands<D>(vcur + 32 * D * 2, voff, va);
+  pv_mfma<D, QB>(st, va, p1);
 }
 
 template <int D, int QB>
@@ -352,49 +461,45 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const int row_bytes = (int)(rs * 2);   // the host keeps 64 rows within int range
   char* const kring = reinterpret_cast<char*>(ks);
   char* const vring = reinterpret_cast<char*>(vs);
-  auto issue_stage = [&](int stage) {
+  int src_k[C::CPT], src_v[C::CPT];      // logical source offsets of this lane's chunks
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int P = (wave * C::CPT + i) * 64 + lane;
+    src_k[i] = logical_src<D, true>(P, row_bytes);
+    src_v[i] = logical_src<D, false>(P, row_bytes);
+  }
+  auto issue_fn = [&](char* kdst, char* vdst, int stage) {
     const int kb = stage * kBN;
     const int rows = (L - kb < kBN) ? (L - kb) : kBN;
     const int nrec = rows * row_bytes;
-    __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
-    __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
-    char* kdst = kring + (stage % kStages) * C::TILE_BYTES + wave * C::CPT * 1024;
-    char* vdst = vring + (stage % kStages) * C::TILE_BYTES + wave * C::CPT * 1024;
+    __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+    kdst += wave * C::CPT * 1024;
+    vdst += wave * C::CPT * 1024;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int P = (wave * C::CPT + i) * 64 + lane;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16,
-                                               logical_src<D, true>(P, row_bytes), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16,
-                                               logical_src<D, false>(P, row_bytes), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16, src_k[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
     }
   };
-  auto kstage = [&](int stage, int sb) -> const char* {
-    return kring + (stage % kStages) * C::TILE_BYTES + sb * 32 * D * 2;
-  };
-  auto vstage = [&](int stage, int sb) -> const char* {
-    return vring + (stage % kStages) * C::TILE_BYTES + sb * 32 * D * 2;
-  };
 
-  // ---- stage loop.  Stage s sits in slot s % kStages; the loads of stage s+1 are
-  // issued right after the barrier that retires every reader of its slot, and have the
-  // whole of stage s to land.
-  issue_stage(0);
-  f32x16 s0[QB], s1[QB];
-  bf16x8 p0[QB][2], p1[QB][2];
-  for (int s = 0; s < ns; ++s) {
-    const int key0 = s * kBN;
+  // ---- stage loop.  Stage s sits in slot s % 2; the loads of stage s+1 are issued
+  // right after the barrier that retires every reader of its slot, and have the whole of
+  // stage s to land.  Unrolled by two so both slot offsets are immediates.
+  static_assert(kStages == 2, "the stage loop alternates two slots");
+  issue_fn(kring, vring, 0);
+  for (int s = 0; s < ns; s += 2) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    if (s + 1 < ns) issue_stage(s + 1);
-    qk_subblock<D, QB>(kstage(s, 0), koff, st.qr, s0);
-    qk_subblock<D, QB>(kstage(s, 1), koff, st.qr, s1);
-    softmax_subblock<D, QB>(st, s0, p0, key0, L, c, g);
-    pv_subblock<D, QB>(st, vstage(s, 0), voff, p0);
-    softmax_subblock<D, QB>(st, s1, p1, key0 + 32, L, c, g);
-    pv_subblock<D, QB>(st, vstage(s, 1), voff, p1);
+    stage_body<D, QB>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+                      issue_fn, s, L, koff, voff, c, g);
+    if (s + 1 >= ns) break;
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __syncthreads();
+    stage_body<D, QB>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+                      issue_fn, s + 1, L, koff, voff, c, g);
   }
   __syncthreads();   // the next tile's first stage overwrites slot 0
 
@@ -506,10 +611,10 @@ std::atomic<int> g_occ[kMaxDevices][kVariants];
 int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
 
 #ifndef PFA_D64_QB
-#define PFA_D64_QB 1
+#define PFA_D64_QB 2
 #endif
 #ifndef PFA_D64_WPE
-#define PFA_D64_WPE 4
+#define PFA_D64_WPE 2
 #endif
 #ifndef PFA_D128_QB
 #define PFA_D128_QB 1

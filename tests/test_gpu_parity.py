@@ -190,3 +190,12 @@ def test_sharp_softmax_heads():
     """C4's per-head Q/K scaling at a small size: logits with std up to 4."""
     wl = W.make([1024, 700], 24, 128, seed=71, per_head_qk_scale=True, name="sharp")
     _full_check(wl, "sharp heads [1024,700] H24")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [1.0, 3.0])
+def test_running_max_jumps_inside_a_stage(d, scale):
+    """Large scales make the running max jump by more than 2^8 in many sub-blocks (both
+    halves of a 64-key stage), exercising every rescale path of the online softmax."""
+    wl = W.make([37, 100, 300, 64, 129], 3, d, seed=81, scale=scale, name="max jumps")
+    _full_check(wl, f"max jumps d={d} scale={scale}")
