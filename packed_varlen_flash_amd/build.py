@@ -27,7 +27,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-fvisibility=hidden", "-I", INCLUDE,
+           "-fvisibility=hidden", "-fno-honor-nans", "-I", INCLUDE,
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            SRC, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)

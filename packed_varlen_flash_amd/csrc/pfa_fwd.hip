@@ -44,8 +44,6 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWave * kWaves;
 constexpr int kBN = 64;          // keys per LDS stage
 constexpr int kStages = 2;       // LDS ring depth (stages)
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
@@ -74,17 +72,19 @@ struct Params {
   float c;         // scale * log2(e)
 };
 
-template <int D, int QB>
+// D: head_dim; QB: 32-query blocks per wave; NW: waves per workgroup.
+template <int D, int QB, int NW = 4>
 struct Tile {
-  static constexpr int BM = kWaves * QB * 32;       // query rows per workgroup tile
+  static constexpr int THREADS = kWave * NW;
+  static constexpr int BM = NW * QB * 32;           // query rows per workgroup tile
   static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   static constexpr int TILE_BYTES = kBN * D * 2;    // one K (or V) stage, unpadded
-  static constexpr int CPT = kBN * CPR / kThreads;  // chunks per thread per stage
+  static constexpr int CPT = kBN * CPR / THREADS;   // chunks per thread per stage
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
   static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
-  static_assert(CPT * kThreads == kBN * CPR, "stage must split evenly");
+  static_assert(CPT * THREADS == kBN * CPR, "stage must split evenly");
   static_assert(sizeof(int) * kSortMax <= (size_t)kStages * TILE_BYTES, "len scratch fits");
 };
 
@@ -131,16 +131,16 @@ __device__ __forceinline__ float partner_sum(float x) {
 // Sorted mode (num_seqs <= kSortMax): s_order[r] = segment of rank r (length
 // descending, ties by index), s_prefix[r] = first item of rank r; items of one segment
 // are ordered head-major, query-tile-minor.  Returns the item count.
-template <int BM>
+template <int BM, int THREADS>
 __device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_prefix) {
   const int n = p.num_seqs;
   const int tid = threadIdx.x;
-  for (int s = tid; s < n; s += kThreads) {
+  for (int s = tid; s < n; s += THREADS) {
     int L = p.cu[s + 1] - p.cu[s];
     s_len[s] = L > 0 ? L : 0;
   }
   __syncthreads();
-  for (int s = tid; s < n; s += kThreads) {
+  for (int s = tid; s < n; s += THREADS) {
     const int L = s_len[s];
     int rank = 0;
     for (int t = 0; t < n; ++t) {
@@ -151,23 +151,23 @@ __device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_
   }
   __syncthreads();
   // items per rank, then an inclusive Hillis-Steele scan in place (n <= kSortMax)
-  for (int r = tid; r < n; r += kThreads) {
+  for (int r = tid; r < n; r += THREADS) {
     const int L = s_len[s_order[r]];
     s_prefix[r + 1] = p.heads * ((L + BM - 1) / BM);
   }
   if (tid == 0) s_prefix[0] = 0;
   __syncthreads();
   for (int off = 1; off < n; off <<= 1) {
-    int add[kSortMax / kThreads];
+    int add[kSortMax / THREADS];
 #pragma unroll
-    for (int j = 0; j < kSortMax / kThreads; ++j) {
-      const int r = tid + j * kThreads;
+    for (int j = 0; j < kSortMax / THREADS; ++j) {
+      const int r = tid + j * THREADS;
       add[j] = (r < n && r >= off) ? s_prefix[r + 1 - off] : 0;
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kSortMax / kThreads; ++j) {
-      const int r = tid + j * kThreads;
+    for (int j = 0; j < kSortMax / THREADS; ++j) {
+      const int r = tid + j * THREADS;
       if (r < n) s_prefix[r + 1] += add[j];
     }
     __syncthreads();
@@ -301,12 +301,12 @@ __device__ __forceinline__ bool softmax_head(TileState<D, QB>& st, f32x16 (&s)[Q
   return moved;
 }
 
-// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and the
-// two row sums.  l_run adds the fp32 weights before rounding and gives the LSE (a sum of
-// rounded weights carries up to 2^-9 relative error into the LSE of a sharp row).  l_rnd
-// adds the bf16 weights the PV product actually uses and normalises O, so in a row
-// dominated by one key that key's rounding cancels between numerator and denominator.
-// The bf16 dot accumulates into fresh 8-step partials only.
+// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
+// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of rounded weights can
+// carry up to 2^-9 relative error into the LSE of a sharp row).  l_rnd adds the bf16
+// weights the PV product actually uses and normalises O: the rounding of each weight then
+// enters numerator and denominator alike, which measurably tightens the worst output error
+// on sharp rows.  The bf16 dot accumulates into fresh 8-step partials only.
 template <int D, int QB>
 __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
                                              bf16x8 (&pb)[QB][2], float c) {
@@ -407,13 +407,13 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
   pv_mfma<D, QB>(st, va, p1);
 }
 
-template <int D, int QB>
+template <int D, int QB, int NW>
 __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int seg_a,
                                              int L, int h, int qt, int T) {
-  using C = Tile<D, QB>;
+  using C = Tile<D, QB, NW>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int n32 = lane & 31;         // query column (S^T) / key row of the K operand
   const int g = lane >> 5;           // half-wave
   const int i16 = lane & 15;
@@ -528,10 +528,10 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
 }
 
-template <int D, int QB, int WPE>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+template <int D, int QB, int NW, int WPE>
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 pfa_fwd_kernel(Params p) {
-  using C = Tile<D, QB>;
+  using C = Tile<D, QB, NW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
   __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
@@ -543,7 +543,7 @@ pfa_fwd_kernel(Params p) {
   const bool sorted = p.num_seqs <= kSortMax;
   int total;
   if (sorted) {
-    total = build_schedule<C::BM>(p, s_len, s_order, s_prefix);
+    total = build_schedule<C::BM, C::THREADS>(p, s_len, s_order, s_prefix);
   } else {
     total = p.num_seqs * p.heads * p.qt_max;
   }
@@ -584,7 +584,7 @@ pfa_fwd_kernel(Params p) {
     if (a < 0 || a >= T) continue;
     if (L > T - a) L = T - a;
     if (L <= 0 || qt * C::BM >= L) continue;
-    process_tile<D, QB>(p, ks, vs, a, L, h, qt, T);
+    process_tile<D, QB, NW>(p, ks, vs, a, L, h, qt, T);
   }
 }
 
@@ -594,13 +594,15 @@ pfa_fwd_kernel(Params p) {
 struct Variant {
   const void* fn;
   int bm;
+  int threads;
   size_t lds;
 };
 
-template <int D, int QB, int WPE>
+template <int D, int QB, int NW, int WPE>
 Variant make_variant() {
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, WPE>), Tile<D, QB>::BM,
-                 Tile<D, QB>::LDS_BYTES};
+  using C = Tile<D, QB, NW>;
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, WPE>), C::BM, C::THREADS,
+                 C::LDS_BYTES};
 }
 
 constexpr int kMaxDevices = 64;
@@ -622,10 +624,16 @@ int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
 #ifndef PFA_D128_WPE
 #define PFA_D128_WPE 2
 #endif
+#ifndef PFA_D64_NW
+#define PFA_D64_NW 4
+#endif
+#ifndef PFA_D128_NW
+#define PFA_D128_NW 8
+#endif
 
 Variant variant_for(int head_dim) {
-  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_WPE>();
-  return make_variant<128, PFA_D128_QB, PFA_D128_WPE>();
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_WPE>();
+  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_WPE>();
 }
 
 }  // namespace
@@ -699,7 +707,7 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
     if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)var.lds) != hipSuccess)
       return PFA_ERR_DEVICE;
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, kThreads, var.lds) != hipSuccess || o <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, var.threads, var.lds) != hipSuccess || o <= 0)
       return PFA_ERR_DEVICE;
     occ = o;
     g_occ[dev][vi].store(occ, std::memory_order_relaxed);
@@ -721,7 +729,7 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
   prm.qt_max = (int)qt_max;
   prm.c = scale * kLog2e;
   void* args[] = {&prm};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(kThreads), args, var.lds, stream);
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, var.lds, stream);
   return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 
