@@ -44,7 +44,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWave = 64;
-constexpr int kBN = 64;          // keys per LDS stage
+constexpr int kHalf = 64;        // keys per softmax step (two 32-key sub-blocks)
 constexpr int kStages = 2;       // LDS ring depth (stages)
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
 constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
@@ -72,19 +72,21 @@ struct Params {
   float c;         // scale * log2(e)
 };
 
-// D: head_dim; QB: 32-query blocks per wave; NW: waves per workgroup.
-template <int D, int QB, int NW = 4>
+// D: head_dim; QB: 32-query blocks per wave; NW: waves per workgroup; SK: keys per LDS
+// stage (a multiple of 64).
+template <int D, int QB, int NW = 4, int SK = 64>
 struct Tile {
   static constexpr int THREADS = kWave * NW;
   static constexpr int BM = NW * QB * 32;           // query rows per workgroup tile
   static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  static constexpr int TILE_BYTES = kBN * D * 2;    // one K (or V) stage, unpadded
-  static constexpr int CPT = kBN * CPR / THREADS;   // chunks per thread per stage
+  static constexpr int TILE_BYTES = SK * D * 2;     // one K (or V) stage, unpadded
+  static constexpr int CPT = SK * CPR / THREADS;    // chunks per thread per stage
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
   static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
-  static_assert(CPT * THREADS == kBN * CPR, "stage must split evenly");
+  static_assert(CPT * THREADS == SK * CPR, "stage must split evenly");
+  static_assert(SK % kHalf == 0, "stages hold whole 64-key halves");
   static_assert(sizeof(int) * kSortMax <= (size_t)kStages * TILE_BYTES, "len scratch fits");
 };
 
@@ -252,34 +254,30 @@ __device__ __forceinline__ void pv_mfma(TileState<D, QB>& st, const bf16x8 (&va)
         st.o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][dt], pb[b][cc], st.o[b][dt], 0, 0, 0);
 }
 
-// Online softmax, first half: mask keys past the segment end, take the block max and move
-// the running max when it is exceeded by more than kRescaleSlack.  Until then
-// P = 2^(s*c - m) <= 2^slack and O, l keep their scale, which is exact: the final O/l and
-// LSE use the same m.  A fully masked block has max -inf.  The row sums are rescaled at once;
-// O is rescaled here only when no weights computed against the old max are still waiting
-// to be added (DEFER_O false).  Otherwise the factor is returned in alpha (1 when the max
-// did not move) and the caller applies it after those weights have been accumulated.
-template <int D, int QB, bool DEFER_O>
-__device__ __forceinline__ bool softmax_head(TileState<D, QB>& st, f32x16 (&s)[QB], int key0,
-                                             int L, float c, int g, float (&alpha)[QB]) {
+// Online softmax head over a whole 64-key stage (both sub-blocks): one max, one rescale
+// decision.  No weights are pending when it runs, so O is rescaled in place.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0)[QB],
+                                               f32x16 (&s1)[QB], int key0, int L, float c, int g) {
   using C = Tile<D, QB>;
-  if (key0 + 32 > L) {
+  if (key0 + 64 > L) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
-      if (key >= L) {
 #pragma unroll
-        for (int b = 0; b < QB; ++b) s[b][i] = -INFINITY;
+      for (int b = 0; b < QB; ++b) {
+        if (key >= L) s0[b][i] = -INFINITY;
+        if (key + 32 >= L) s1[b][i] = -INFINITY;
       }
     }
   }
-  bool moved = false;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    alpha[b] = 1.f;
-    float mx = fmaxf(s[b][0], s[b][1]);
+    float mx = fmaxf(s0[b][0], s0[b][1]);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s0[b][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[b][i]);
     mx = partner_max(mx);
     const float mb = mx * c;
     if (__builtin_amdgcn_ballot_w64(mb > st.m_run[b] + kRescaleSlack) != 0) {
@@ -288,17 +286,12 @@ __device__ __forceinline__ bool softmax_head(TileState<D, QB>& st, f32x16 (&s)[Q
       st.m_run[b] = m_new;
       st.l_run[b] *= a;
       st.l_rnd[b] *= a;
-      alpha[b] = a;
-      moved = true;
-      if (!DEFER_O) {
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= a;
-      }
+        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= a;
     }
   }
-  return moved;
 }
 
 // Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
@@ -333,23 +326,6 @@ __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 
   }
 }
 
-// Keeps the bf16 weights and row sums of a softmax body where they are computed: without
-// it the compiler sinks them past the next branch, next to their use, which separates
-// them from the MFMAs they are meant to run beside.  Emits no instruction.
-template <int D, int QB>
-__device__ __forceinline__ void pin_softmax(TileState<D, QB>& st, bf16x8 (&pb)[QB][2]) {
-#pragma unroll
-  for (int b = 0; b < QB; ++b) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      u32x4 w = __builtin_bit_cast(u32x4, pb[b][cc]);
-      asm volatile("" : "+v"(w));
-      pb[b][cc] = __builtin_bit_cast(bf16x8, w);
-    }
-    asm volatile("" : "+v"(st.l_run[b]), "+v"(st.l_rnd[b]));
-  }
-}
-
 // Interleave n MFMAs with the VALU work around them, `valu` VALU instructions after each.
 template <int N, int VALU>
 __device__ __forceinline__ void interleave_mfma_valu() {
@@ -366,7 +342,7 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // from waiting on the next slot's loads.  The straight-line half of each sub-block's
 // softmax shares a basic block with the MFMAs of the neighbouring sub-block (QK of the
 // next, PV of the previous), so the MFMA pipe and the VALU work side by side.
-template <int D, int QB, typename IssueFn>
+template <int D, int QB, int SK, typename IssueFn>
 __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restrict__ knext,
                                            char* __restrict__ vnext, const char* __restrict__ kcur,
                                            const char* __restrict__ vcur, bool issue,
@@ -375,42 +351,35 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
                                            float c, int g) {
   constexpr int NQK = QB * D / 16;   // MFMAs of one sub-block's QK (and of its PV)
   if (issue) issue_fn(knext, vnext, s + 1);
-  const int key0 = s * kBN;
-  f32x16 s0[QB], s1[QB];
-  bf16x8 p0[QB][2], p1[QB][2];
-  bf16x8 ka[D / 16], kb[D / 16];
-  bf16x8 va[2][D / 32];
-  float alpha[QB];
-  k_operands<D>(kcur, koff, ka);
-  qk_mfma<D, QB>(ka, st.qr, s0);
-  k_operands<D>(kcur + 32 * D * 2, koff, kb);
-  softmax_head<D, QB, false>(st, s0, key0, L, c, g, alpha);
-  qk_mfma<D, QB>(kb, st.qr, s1);
-  softmax_body<D, QB>(st, s0, p0, c);
-  interleave_mfma_valu<NQK, 8 * 16 / NQK>();
-  pin_softmax<D, QB>(st, p0);
-  v_operands<D>(vcur, voff, va);
-  // P0 was computed against the max before this head: O's rescale waits until P0 V is in
-  const bool moved = softmax_head<D, QB, true>(st, s1, key0 + 32, L, c, g, alpha);
-  pv_mfma<D, QB>(st, va, p0);
-  softmax_body<D, QB>(st, s1, p1, c);
-  interleave_mfma_valu<NQK, 8 * 16 / NQK>();
-  if (moved) {
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= alpha[b];
+  for (int half = 0; half < SK / kHalf; ++half) {
+    const int key0 = s * SK + half * kHalf;
+    if (half > 0 && key0 >= L) break;            // nothing left in this stage
+    const char* kh = kcur + half * kHalf * D * 2;
+    const char* vh = vcur + half * kHalf * D * 2;
+    f32x16 s0[QB], s1[QB];
+    bf16x8 p0[QB][2], p1[QB][2];
+    bf16x8 ka[D / 16], kb[D / 16];
+    bf16x8 va[2][D / 32];
+    k_operands<D>(kh, koff, ka);
+    qk_mfma<D, QB>(ka, st.qr, s0);
+    k_operands<D>(kh + 32 * D * 2, koff, kb);
+    qk_mfma<D, QB>(kb, st.qr, s1);
+    softmax_head64<D, QB>(st, s0, s1, key0, L, c, g);
+    softmax_body<D, QB>(st, s0, p0, c);
+    v_operands<D>(vh, voff, va);
+    pv_mfma<D, QB>(st, va, p0);
+    softmax_body<D, QB>(st, s1, p1, c);
+    interleave_mfma_valu<NQK, 8 * 16 / NQK>();
+    v_operands<D>(vh + 32 * D * 2, voff, va);
+    pv_mfma<D, QB>(st, va, p1);
   }
-  v_operands<D>(vcur + 32 * D * 2, voff, va);
-  pv_mfma<D, QB>(st, va, p1);
 }
 
-template <int D, int QB, int NW>
+template <int D, int QB, int NW, int SK>
 __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int seg_a,
                                              int L, int h, int qt, int T) {
-  using C = Tile<D, QB, NW>;
+  using C = Tile<D, QB, NW, SK>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -424,7 +393,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const __bf16* kbase = p.k + (int64_t)seg_a * rs + head_off;
   const __bf16* vbase = p.v + (int64_t)seg_a * rs + head_off;
   const int q0 = qt * C::BM + wave * (QB * 32);
-  const int ns = (L + kBN - 1) / kBN;      // 64-key stages
+  const int ns = (L + SK - 1) / SK;        // LDS stages
   const float c = p.c;
 
   TileState<D, QB> st;
@@ -469,8 +438,8 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     src_v[i] = logical_src<D, false>(P, row_bytes);
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
-    const int kb = stage * kBN;
-    const int rows = (L - kb < kBN) ? (L - kb) : kBN;
+    const int kb = stage * SK;
+    const int rows = (L - kb < SK) ? (L - kb) : SK;
     const int nrec = rows * row_bytes;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
@@ -493,12 +462,12 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   for (int s = 0; s < ns; s += 2) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    stage_body<D, QB>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+    stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
                       issue_fn, s, L, koff, voff, c, g);
     if (s + 1 >= ns) break;
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    stage_body<D, QB>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+    stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
                       issue_fn, s + 1, L, koff, voff, c, g);
   }
   __syncthreads();   // the next tile's first stage overwrites slot 0
@@ -528,10 +497,10 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
 }
 
-template <int D, int QB, int NW, int WPE>
+template <int D, int QB, int NW, int SK, int WPE>
 __global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 pfa_fwd_kernel(Params p) {
-  using C = Tile<D, QB, NW>;
+  using C = Tile<D, QB, NW, SK>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
   __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
@@ -584,7 +553,7 @@ pfa_fwd_kernel(Params p) {
     if (a < 0 || a >= T) continue;
     if (L > T - a) L = T - a;
     if (L <= 0 || qt * C::BM >= L) continue;
-    process_tile<D, QB, NW>(p, ks, vs, a, L, h, qt, T);
+    process_tile<D, QB, NW, SK>(p, ks, vs, a, L, h, qt, T);
   }
 }
 
@@ -598,11 +567,11 @@ struct Variant {
   size_t lds;
 };
 
-template <int D, int QB, int NW, int WPE>
+template <int D, int QB, int NW, int SK, int WPE>
 Variant make_variant() {
-  using C = Tile<D, QB, NW>;
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, WPE>), C::BM, C::THREADS,
-                 C::LDS_BYTES};
+  using C = Tile<D, QB, NW, SK>;
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE>), C::BM,
+                 C::THREADS, C::LDS_BYTES};
 }
 
 constexpr int kMaxDevices = 64;
@@ -630,10 +599,16 @@ int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
 #ifndef PFA_D128_NW
 #define PFA_D128_NW 8
 #endif
+#ifndef PFA_D64_SK
+#define PFA_D64_SK 64
+#endif
+#ifndef PFA_D128_SK
+#define PFA_D128_SK 64
+#endif
 
 Variant variant_for(int head_dim) {
-  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_WPE>();
-  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_WPE>();
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE>();
+  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE>();
 }
 
 }  // namespace
