@@ -33,23 +33,23 @@ import pfa_workloads as W  # noqa: E402
 
 METRIC = "attention TFLOP/s (4·ΣL_i²·H·d) and % of bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0            # MI355X dense bf16 MFMA (published)
-KERNEL_SRC = os.path.join(ROOT, "packed_varlen_flash_amd", "csrc", "pfa_fwd.hip")
+LIBRARY = os.path.join(ROOT, "packed_varlen_flash_amd", "libpfa.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pfa_fwd_C3.json")
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def library_sha() -> str:
+    with open(LIBRARY, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
 def measured_traffic(config: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken
-    on the kernel source as it is now; otherwise None."""
-    if config != "C3" or not os.path.exists(TRAFFIC_FILE):
+    on the library binary as it is now (the build is deterministic); otherwise None."""
+    if config != "C3" or not os.path.exists(TRAFFIC_FILE) or not os.path.exists(LIBRARY):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_sha256") != kernel_sha():
+    if t.get("library_sha256") != library_sha():
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -9,14 +9,16 @@
 // running row maximum and normaliser, rescale and accumulate the output, and write only
 // the final output (and here the log-sum-exp) back to HBM.
 //
-// gfx950 mapping (one workgroup = 4 wave64s, one wave per SIMD):
+// gfx950 mapping (d = 128: one workgroup = 8 wave64s on one CU, two waves per SIMD;
+// d = 64: 4 wave64s):
 //   * work unit = (segment, head, BM-row query tile); a tile never spans two segments.
 //     Tiles are listed longest segment first and handed out round-robin by a persistent
 //     grid; each XCD receives contiguous runs of the list so the query tiles that share
 //     one (segment, head) K/V stream sit behind the same L2.
 //   * each wave owns QB blocks of 32 queries and keeps their Q fragments in VGPRs.
-//   * K and V tiles of 64 keys are double-buffered in LDS, loaded with 16-byte global
-//     loads; rows past the segment end are zero-filled, never read from a neighbour.
+//   * K and V stages of 64 keys are double-buffered in LDS, loaded global -> LDS directly
+//     by buffer loads bounded at the segment end, so rows past it read as zeros and no
+//     neighbouring segment is ever touched.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the accumulator gives every lane one
 //     query column, so the row maximum and row sum are in-lane reductions plus a single
 //     v_permlane32_swap between the two half-waves.
@@ -180,15 +182,12 @@ __device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_
 // ---------------------------------------------------------------------------------
 // One query tile of one (segment, head).
 //
-// Keys are consumed in 32-key sub-blocks; LDS holds a ring of kStages 64-key stages.
-// Per stage s (sub-blocks 2s and 2s+1) the wave runs, in program order,
-//   A: S1 = K(2s+1) Q^T          with the softmax of S0 (sub-block 2s) interleaved
-//   B: O += V(2s)^T P0
-//   -- workgroup barrier --
-//   C: S0 = K(2s+2) Q^T          with the softmax of S1 interleaved; stage s+2 -> LDS
-//   D: O += V(2s+1)^T P1
-// so the MFMA pipe always has independent work while the softmax VALU runs.  Stage
-// s+2 overwrites the slot of stage s-1, whose last readers finished before the barrier.
+// Keys are consumed in 64-key LDS stages held in a ring of kStages slots.  Per stage the
+// wave computes both 32-key sub-blocks of S^T = K Q^T, runs one softmax head over the 64
+// keys (mask, max, rescale decision), then the weights of sub-block 0, its PV product,
+// the weights of sub-block 1 interleaved with that product's MFMAs, and the second PV.
+// The loads of stage s+1 are issued right after the barrier that opens stage s, into the
+// slot whose last readers that barrier retired.
 // ---------------------------------------------------------------------------------
 template <int D, int QB>
 struct TileState {
