@@ -208,19 +208,26 @@ __device__ __forceinline__ void k_operands(const char* kst, const int (&koff)[D 
   for (int t = 0; t < D / 16; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
 }
 
-// S^T (keys x queries) = K Q^T for one sub-block.
+// S^T (keys x queries) = K Q^T for both 32-key sub-blocks of a stage, the two accumulator
+// chains interleaved so consecutive MFMAs never depend on each other.
 template <int D, int QB>
-__device__ __forceinline__ void qk_mfma(const bf16x8 (&a)[D / 16], const bf16x8 (&qr)[QB][D / 16],
-                                        f32x16 (&s)[QB]) {
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&ka)[D / 16], const bf16x8 (&kb)[D / 16],
+                                        const bf16x8 (&qr)[QB][D / 16], f32x16 (&s0)[QB],
+                                        f32x16 (&s1)[QB]) {
 #pragma unroll
   for (int b = 0; b < QB; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[b][i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      s0[b][i] = 0.f;
+      s1[b][i] = 0.f;
+    }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t)
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
-      s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], qr[b][t], s[b], 0, 0, 0);
+    for (int b = 0; b < QB; ++b) {
+      s0[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], qr[b][t], s0[b], 0, 0, 0);
+      s1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t], qr[b][t], s1[b], 0, 0, 0);
+    }
 }
 
 // V^T operand fragments of one sub-block: vst points at its first row; voff[dt] is this
@@ -298,30 +305,25 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
 // carry up to 2^-9 relative error into the LSE of a sharp row).  l_rnd adds the bf16
 // weights the PV product actually uses and normalises O: the rounding of each weight then
 // enters numerator and denominator alike, which measurably tightens the worst output error
-// on sharp rows.  The bf16 dot accumulates into fresh 8-step partials only.
+// on sharp rows.  Both sums chain straight into their running values (one add, resp. one
+// bf16 dot of a weight pair, per step), with no partial sums to seed or combine.
 template <int D, int QB>
 __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
                                              bf16x8 (&pb)[QB][2], float c) {
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float neg_m = -st.m_run[b];
-    float ex0 = 0.f, ex1 = 0.f, rd0 = 0.f, rd1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float e0 = __builtin_amdgcn_exp2f(fmaf(s[b][i], c, neg_m));
       const float e1 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 1], c, neg_m));
-      ex0 += e0;
-      ex1 += e1;
+      st.l_run[b] += e0;
+      st.l_run[b] += e1;
       const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-      if (i < 8)
-        rd0 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rd0, false);
-      else
-        rd1 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, rd1, false);
+      st.l_rnd[b] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, st.l_rnd[b], false);
       pb[b][i >> 3][i & 7] = pr[0];
       pb[b][i >> 3][(i & 7) + 1] = pr[1];
     }
-    st.l_run[b] += ex0 + ex1;
-    st.l_rnd[b] += rd0 + rd1;
   }
 }
 
@@ -361,9 +363,8 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
     bf16x8 ka[D / 16], kb[D / 16];
     bf16x8 va[2][D / 32];
     k_operands<D>(kh, koff, ka);
-    qk_mfma<D, QB>(ka, st.qr, s0);
     k_operands<D>(kh + 32 * D * 2, koff, kb);
-    qk_mfma<D, QB>(kb, st.qr, s1);
+    qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
     softmax_head64<D, QB>(st, s0, s1, key0, L, c, g);
     softmax_body<D, QB>(st, s0, p0, c);
     v_operands<D>(vh, voff, va);
