@@ -470,31 +470,45 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
                       issue_fn, s + 1, L, koff, voff, c, g);
   }
-  __syncthreads();   // the next tile's first stage overwrites slot 0
+  __syncthreads();   // every wave has left the ring
 
-  // ---- epilogue: O = acc / l_rnd in bf16 (round to nearest even),
-  //      LSE = ln2 * (m + log2 l_run)
+  // ---- epilogue: O = acc / l_rnd in bf16 (round to nearest even), LSE = ln2 * (m + log2
+  // l_run).  O goes out through LDS: each wave writes its (QB*32) x D block into the free
+  // ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
+  // consecutive rows, so 16 lanes store 256 contiguous bytes instead of every store
+  // instruction touching 16-byte pieces of 32 different rows.
+  static_assert(NW * QB * 32 * D * 2 <= 2 * kStages * C::TILE_BYTES, "O staging fits the ring");
+  char* const ost = kring + wave * (QB * 32 * D * 2);
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = partner_sum(st.l_run[b]);
-    const float lr = partner_sum(st.l_rnd[b]);
-    const int row = q0 + b * 32 + n32;
-    if (row < L) {
-      const float inv = 1.0f / lr;
-      __bf16* orow = p.out + (int64_t)(seg_a + row) * rs + head_off;
+    const float inv = 1.0f / partner_sum(st.l_rnd[b]);
+    const int r = b * 32 + n32;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          bf16x4 w;
+      for (int ii = 0; ii < 4; ++ii) {
+        bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * ii + 4 * g) = w;
-        }
-      if (p.lse != nullptr && g == 0)
-        p.lse[(int64_t)h * T + seg_a + row] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
-    }
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv);
+        *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(r, 4 * dt + ii) + 8 * g) = w;
+      }
+    if (p.lse != nullptr && g == 0 && q0 + r < L)
+      p.lse[(int64_t)h * T + seg_a + q0 + r] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
+  __syncthreads();
+  constexpr int OCH = QB * 32 * C::CPR;      // 16-byte chunks of the wave's block
+  static_assert(OCH % kWave == 0, "whole chunk rows per lane");
+#pragma unroll
+  for (int k = 0; k < OCH / kWave; ++k) {
+    const int P = k * kWave + lane;
+    const int r = P / C::CPR;
+    const int ch = P % C::CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, true>(r, ch));
+    if (q0 + r < L)
+      *reinterpret_cast<u32x4*>(p.out + (int64_t)(seg_a + q0 + r) * rs + head_off + ch * 8) = x;
+  }
+  __syncthreads();   // the next tile's first stage overwrites the ring
 }
 
 template <int D, int QB, int NW, int SK, int WPE>
