@@ -10,6 +10,11 @@ marshals:
 * ``varlen_fwd(q, k, v, cu_seqlens, scale, rows=None)`` -> ``(out, lse)``:
   ``out`` is ``[T, H, dv]`` fp64 and ``lse`` is ``[H, T]`` fp64 (natural log), or
   ``[n, H, dv]`` / ``[H, n]`` for a row sample ``rows``.
+* ``varlen_fwd_qk(q, k, v, cu_q, cu_k, scale, rows=None)``: the same with separate query
+  and key tables (queries of segment s attend the keys of segment s); a segment with
+  queries but no keys gives a zero output and ``lse = -inf``.
+* ``merge(o_a, lse_a, o_b, lse_b)`` -> ``(o, lse)``: attention over the union of two
+  disjoint key sets from the results over each (fp64, see its docstring).
 * ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
   probability matrix over all ``T`` tokens (zero off-segment).
 
@@ -54,6 +59,9 @@ def _load():
         vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.pfa_oracle_fwd.argtypes = [i32, vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64, vp, vp]
         lib.pfa_oracle_fwd.restype = i32
+        lib.pfa_oracle_fwd_qk.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64,
+                                          vp, vp]
+        lib.pfa_oracle_fwd_qk.restype = i32
         lib.pfa_oracle_probs.argtypes = [i32, vp, vp, vp, i32, i32, i32, f64, i64, i32, vp]
         lib.pfa_oracle_probs.restype = i32
         lib.pfa_oracle_num_threads.argtypes = []
@@ -103,6 +111,65 @@ def varlen_fwd(q, k, v, cu_seqlens, scale: float, rows=None):
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, lse
+
+
+def varlen_fwd_qk(q, k, v, cu_q, cu_k, scale: float, rows=None):
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    kind = _kind(q)
+    if _kind(k) != kind or _kind(v) != kind:
+        raise TypeError("q, k and v must share one element type")
+    if q.ndim != 3 or k.ndim != 3 or v.ndim != 3 or k.shape[1:] != q.shape[1:] \
+            or v.shape[:2] != k.shape[:2]:
+        raise ValueError("expected q [Tq, H, d], k [Tk, H, d] and v [Tk, H, dv]")
+    cq = np.ascontiguousarray(cu_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_k, dtype=np.int32)
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    dv = v.shape[2]
+    num_seqs = cq.shape[0] - 1
+    if num_seqs < 1 or ck.shape[0] != cq.shape[0] or int(cq[-1]) != Tq or int(ck[-1]) != Tk:
+        raise ValueError("cu_q / cu_k must have the same length >= 2 and end at Tq / Tk")
+    if rows is None:
+        n = Tq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.shape[0]
+    out = np.empty((n, H, dv), dtype=np.float64)
+    lse = np.empty((H, n), dtype=np.float64)
+    rc = _load().pfa_oracle_fwd_qk(kind, _ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), num_seqs,
+                                   H, d, dv, float(scale),
+                                   _ptr(rows_arr) if rows_arr is not None else None, n,
+                                   _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return out, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b):
+    """Attention over the union of two disjoint key sets A and B, from the results over
+    each: with Z_X = exp(LSE_X) the partition sum over X, the union's partition sum is
+    Z_A + Z_B and its output the Z-weighted mean of O_A and O_B (the identity behind the
+    blocked update of the GigaPath-Flash page, section 3.2, applied to two finished
+    blocks).  o_* are [n, H, dv], lse_* are [H, n]; fp64 throughout.  An empty set has
+    LSE = -inf and contributes nothing; two empty sets give o = 0, lse = -inf."""
+    o_a = np.asarray(o_a, dtype=np.float64)
+    o_b = np.asarray(o_b, dtype=np.float64)
+    la = np.asarray(lse_a, dtype=np.float64)
+    lb = np.asarray(lse_b, dtype=np.float64)
+    m = np.maximum(la, lb)
+    both_empty = np.isneginf(m)
+    ms = np.where(both_empty, 0.0, m)
+    za = np.exp(la - ms)                    # exp(-inf) = 0 for an empty side
+    zb = np.exp(lb - ms)
+    z = za + zb
+    lse = np.where(both_empty, -np.inf, ms + np.log(np.where(both_empty, 1.0, z)))
+    wa = np.where(both_empty, 0.0, za / np.where(both_empty, 1.0, z))
+    wb = np.where(both_empty, 0.0, zb / np.where(both_empty, 1.0, z))
+    o = wa.T[:, :, None] * o_a + wb.T[:, :, None] * o_b
+    return o, lse
 
 
 def probs(q, k, cu_seqlens, scale: float, i: int, h: int):

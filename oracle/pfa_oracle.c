@@ -28,6 +28,15 @@
  *   over only the retained keys.  The retained set here always contains the query
  *   itself, so it is never empty.
  *
+ * Separate query and key tables (pfa_oracle_fwd_qk): the varlen call of the same
+ * listing takes cu_seqlens_q and cu_seqlens_k (and max_seqlen_q / max_seqlen_k) as
+ * separate arguments; with different tables, the queries of segment s are rows
+ * [cu_q[s], cu_q[s+1]) of q and attend exactly the keys [cu_k[s], cu_k[s+1]) of k and v.
+ * That is the cross-attention of the xxmr.cn editing-network article (section 3.1: Q
+ * from the draft features, K and V from the condition or edit sequence; section 4.1:
+ * those sequences are much shorter than the query sequence).  A segment with queries but
+ * no keys has no softmax; the reading taken here is a zero output and LSE = ln 0 = -inf.
+ *
  * Deliberately two-pass (exact row max first, then the sums), not the blocked online
  * recurrence of the GigaPath-Flash page, section 3.2: the oracle must not share the
  * method's algorithm.  All arithmetic is fp64 on the exact input values.
@@ -87,6 +96,11 @@ static void one_row(int kind, const void* q, const void* k, const void* v, int64
                     int64_t i, int h, int heads, int d, int dv, double scale, double* score,
                     double* o, double* lse_out) {
   const int64_t qoff = (i * heads + h) * (int64_t)d;
+  if (b <= a) { /* no keys: zero output, LSE of an empty sum */
+    for (int c = 0; c < dv; ++c) o[c] = 0.0;
+    *lse_out = -INFINITY;
+    return;
+  }
   /* pass 1: scores and their exact maximum */
   double m = -INFINITY;
   for (int64_t j = a; j < b; ++j) {
@@ -117,24 +131,27 @@ static int max_segment_length(const int32_t* cu, int num_seqs) {
 }
 
 /*
- * Full or row-sampled forward.
- *   rows == NULL: every token; out is [T, heads, dv], lse is [heads, T].
- *   rows != NULL: only tokens rows[0..n_rows); out is [n_rows, heads, dv],
+ * Full or row-sampled forward with separate query and key tables.
+ *   q is [Tq, heads, d], k is [Tk, heads, d], v is [Tk, heads, dv], with
+ *   Tq = cu_q[num_seqs] and Tk = cu_k[num_seqs].
+ *   rows == NULL: every query token; out is [Tq, heads, dv], lse is [heads, Tq].
+ *   rows != NULL: only query tokens rows[0..n_rows); out is [n_rows, heads, dv],
  *                 lse is [heads, n_rows].
  * Returns 0, or ORACLE_EINVAL for a malformed table / row index, ORACLE_ENOMEM.
  */
-int pfa_oracle_fwd(int kind, const void* q, const void* k, const void* v, const int32_t* cu,
-                   int num_seqs, int heads, int d, int dv, double scale, const int64_t* rows,
-                   int64_t n_rows, double* out, double* lse) {
+int pfa_oracle_fwd_qk(int kind, const void* q, const void* k, const void* v, const int32_t* cu_q,
+                      const int32_t* cu_k, int num_seqs, int heads, int d, int dv, double scale,
+                      const int64_t* rows, int64_t n_rows, double* out, double* lse) {
   if (kind != ELEM_F64 && kind != ELEM_BF16) return ORACLE_EINVAL;
   if (!q || !k || !v || !out || !lse || heads < 1 || d < 1 || dv < 1) return ORACLE_EINVAL;
-  if (check_table(cu, num_seqs) != ORACLE_OK) return ORACLE_EINVAL;
-  const int64_t total = cu[num_seqs];
+  if (check_table(cu_q, num_seqs) != ORACLE_OK || check_table(cu_k, num_seqs) != ORACLE_OK)
+    return ORACLE_EINVAL;
+  const int64_t total = cu_q[num_seqs];
   const int64_t n = rows ? n_rows : total;
   if (rows)
     for (int64_t r = 0; r < n_rows; ++r)
       if (rows[r] < 0 || rows[r] >= total) return ORACLE_EINVAL;
-  const int maxlen = max_segment_length(cu, num_seqs);
+  const int maxlen = max_segment_length(cu_k, num_seqs);
   int failed = 0;
 #pragma omp parallel
   {
@@ -149,9 +166,9 @@ int pfa_oracle_fwd(int kind, const void* q, const void* k, const void* v, const 
         const int64_t r = w / heads;
         const int h = (int)(w % heads);
         const int64_t i = rows ? rows[r] : r;
-        const int s = owner_segment(cu, num_seqs, i);
+        const int s = owner_segment(cu_q, num_seqs, i);
         double l;
-        one_row(kind, q, k, v, cu[s], cu[s + 1], i, h, heads, d, dv, scale, score, o, &l);
+        one_row(kind, q, k, v, cu_k[s], cu_k[s + 1], i, h, heads, d, dv, scale, score, o, &l);
         memcpy(out + (r * heads + h) * (int64_t)dv, o, sizeof(double) * (size_t)dv);
         lse[(int64_t)h * n + r] = l;
       }
@@ -160,6 +177,15 @@ int pfa_oracle_fwd(int kind, const void* q, const void* k, const void* v, const 
     free(o);
   }
   return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/* Self-attention over one table: queries and keys share cu (the listing passes the same
+ * cu_seqlens for both). */
+int pfa_oracle_fwd(int kind, const void* q, const void* k, const void* v, const int32_t* cu,
+                   int num_seqs, int heads, int d, int dv, double scale, const int64_t* rows,
+                   int64_t n_rows, double* out, double* lse) {
+  return pfa_oracle_fwd_qk(kind, q, k, v, cu, cu, num_seqs, heads, d, dv, scale, rows, n_rows,
+                           out, lse);
 }
 
 /*

@@ -32,3 +32,29 @@ def dense_block_diag(q, k, v, cu, scale):
         out[:, h, :] = (e / z) @ v[:, h, :]
         lse[h] = mx[:, 0] + np.log(z[:, 0])
     return out, lse
+
+
+def dense_block_rect(q, k, v, cu_q, cu_k, scale):
+    """Rectangular variant: query token i of segment s may see key token j only when j
+    lies in segment s of the key table.  A query whose key segment is empty has an
+    all -inf row; it is given output 0 and LSE -inf explicitly (no softmax exists)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Tq, H, _ = q.shape
+    Tk = k.shape[0]
+    sq = segment_ids(cu_q, Tq)
+    sk = segment_ids(cu_k, Tk)
+    allowed = sq[:, None] == sk[None, :]
+    empty = ~allowed.any(axis=1)
+    out = np.zeros((Tq, H, v.shape[2]))
+    lse = np.full((H, Tq), -np.inf)
+    for h in range(H):
+        s = scale * (q[:, h, :] @ k[:, h, :].T)
+        s = np.where(allowed, s, -np.inf)
+        for i in np.nonzero(~empty)[0]:
+            mx = s[i].max()
+            e = np.exp(s[i] - mx)
+            out[i, h, :] = (e / e.sum()) @ v[:, h, :]
+            lse[h, i] = mx + np.log(e.sum())
+    return out, lse

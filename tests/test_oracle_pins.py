@@ -291,3 +291,156 @@ def test_rejects_malformed_tables():
         oracle.varlen_fwd(q, q, v, [0, 3, 2, 4], 1.0)      # decreasing
     with pytest.raises(ValueError):
         oracle.varlen_fwd(q, q, v, [1, 4], 1.0)            # does not start at 0
+
+
+# ---------------------------------------------------------------------------------
+# Separate query / key tables (the varlen call's cu_seqlens_q and cu_seqlens_k) and the
+# (O, LSE) merge of two disjoint key sets.
+# ---------------------------------------------------------------------------------
+from tests._brute import dense_block_rect  # noqa: E402
+
+
+def _rect_case(seed, H=3, d=8, dv=5):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 6))
+    lq = rng.integers(0, 9, size=n)
+    lk = rng.integers(0, 9, size=n)
+    lq[0] = max(lq[0], 1)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = rng.standard_normal((int(cu_q[-1]), H, d))
+    k = rng.standard_normal((int(cu_k[-1]), H, d))
+    v = rng.standard_normal((int(cu_k[-1]), H, dv))
+    return q, k, v, cu_q, cu_k
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_qk_tables_match_dense_rectangular_brute_force(seed):
+    q, k, v, cu_q, cu_k = _rect_case(seed)
+    o, l = oracle.varlen_fwd_qk(q, k, v, cu_q, cu_k, 0.4)
+    ob, lb = dense_block_rect(q, k, v, cu_q, cu_k, 0.4)
+    np.testing.assert_allclose(o, ob, rtol=0, atol=1e-13)
+    finite = np.isfinite(lb)
+    np.testing.assert_array_equal(np.isfinite(l), finite)
+    np.testing.assert_allclose(l[finite], lb[finite], rtol=0, atol=1e-13)
+
+
+def test_qk_tables_match_torch_sdpa_per_segment():
+    rng = np.random.default_rng(3)
+    lq, lk = [37, 5, 64], [7, 90, 1]
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = rng.standard_normal((sum(lq), 2, 16))
+    k = rng.standard_normal((sum(lk), 2, 16))
+    v = rng.standard_normal((sum(lk), 2, 16))
+    o, _ = oracle.varlen_fwd_qk(q, k, v, cu_q, cu_k, 0.25)
+    for s in range(3):
+        qs = torch.from_numpy(q[cu_q[s]:cu_q[s + 1]]).permute(1, 0, 2)
+        ks = torch.from_numpy(k[cu_k[s]:cu_k[s + 1]]).permute(1, 0, 2)
+        vs = torch.from_numpy(v[cu_k[s]:cu_k[s + 1]]).permute(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(qs, ks, vs, scale=0.25)
+        np.testing.assert_allclose(o[cu_q[s]:cu_q[s + 1]], ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_qk_tables_closed_forms():
+    # one key per segment: the output is that key's value and LSE = scale * q.k
+    rng = np.random.default_rng(5)
+    cu_q = np.array([0, 4, 9], np.int32)
+    cu_k = np.array([0, 1, 2], np.int32)
+    q = rng.standard_normal((9, 2, 6))
+    k = rng.standard_normal((2, 2, 6))
+    v = rng.standard_normal((2, 2, 3))
+    o, l = oracle.varlen_fwd_qk(q, k, v, cu_q, cu_k, 0.7)
+    for i in range(9):
+        s = 0 if i < 4 else 1
+        np.testing.assert_array_equal(o[i], v[s])
+        for h in range(2):
+            assert abs(l[h, i] - 0.7 * float(q[i, h] @ k[s, h])) < 1e-14
+    # zero queries: uniform weights over the key segment, LSE = ln(Lk)
+    q0 = np.zeros((9, 2, 6))
+    cu_k2 = np.array([0, 3, 10], np.int32)
+    k2 = rng.standard_normal((10, 2, 6))
+    v2 = rng.standard_normal((10, 2, 3))
+    o, l = oracle.varlen_fwd_qk(q0, k2, v2, cu_q, cu_k2, 1.0)
+    np.testing.assert_allclose(o[:4], np.broadcast_to(v2[:3].mean(axis=0), (4, 2, 3)), atol=1e-15)
+    np.testing.assert_allclose(o[4:], np.broadcast_to(v2[3:].mean(axis=0), (5, 2, 3)), atol=1e-15)
+    np.testing.assert_allclose(l[:, :4], math.log(3), atol=1e-15)
+    np.testing.assert_allclose(l[:, 4:], math.log(7), atol=1e-15)
+
+
+def test_qk_tables_empty_key_segment_gives_zero_and_minus_inf():
+    rng = np.random.default_rng(6)
+    cu_q = np.array([0, 3, 5], np.int32)
+    cu_k = np.array([0, 0, 4], np.int32)
+    q = rng.standard_normal((5, 2, 4))
+    k = rng.standard_normal((4, 2, 4))
+    v = rng.standard_normal((4, 2, 4))
+    o, l = oracle.varlen_fwd_qk(q, k, v, cu_q, cu_k, 1.0)
+    assert np.all(o[:3] == 0.0) and np.all(np.isneginf(l[:, :3]))
+    assert np.all(np.isfinite(l[:, 3:]))
+
+
+def test_qk_tables_with_equal_tables_equal_self_attention():
+    rng = np.random.default_rng(8)
+    cu = np.array([0, 5, 5, 17], np.int32)
+    q, k, v = (rng.standard_normal((17, 2, 8)) for _ in range(3))
+    o1, l1 = oracle.varlen_fwd(q, k, v, cu, 0.3)
+    o2, l2 = oracle.varlen_fwd_qk(q, k, v, cu, cu, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_merge_of_two_key_halves_equals_attention_over_the_union(seed):
+    # keys of each segment split into a first and a second part (either may be empty):
+    # attention over the whole segment = merge of the attentions over the two parts
+    rng = np.random.default_rng(100 + seed)
+    n, H, d, dv = 3, 2, 8, 4
+    lq = rng.integers(1, 7, size=n)
+    la = rng.integers(0, 6, size=n)
+    lb = rng.integers(0, 6, size=n)
+    lb[la + lb == 0] = 1
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    q = rng.standard_normal((int(cu_q[-1]), H, d))
+    ka = [rng.standard_normal((int(x), H, d)) for x in la]
+    kb = [rng.standard_normal((int(x), H, d)) for x in lb]
+    va = [rng.standard_normal((int(x), H, dv)) for x in la]
+    vb = [rng.standard_normal((int(x), H, dv)) for x in lb]
+    cat = lambda parts: np.concatenate(parts, axis=0)
+    cu_a = np.concatenate([[0], np.cumsum(la)]).astype(np.int32)
+    cu_b = np.concatenate([[0], np.cumsum(lb)]).astype(np.int32)
+    cu_u = np.concatenate([[0], np.cumsum(la + lb)]).astype(np.int32)
+    o_a, l_a = oracle.varlen_fwd_qk(q, cat(ka), cat(va), cu_q, cu_a, 0.5)
+    o_b, l_b = oracle.varlen_fwd_qk(q, cat(kb), cat(vb), cu_q, cu_b, 0.5)
+    ku = cat([np.concatenate([a, b]) for a, b in zip(ka, kb)])
+    vu = cat([np.concatenate([a, b]) for a, b in zip(va, vb)])
+    o_u, l_u = oracle.varlen_fwd_qk(q, ku, vu, cu_q, cu_u, 0.5)
+    o_m, l_m = oracle.merge(o_a, l_a, o_b, l_b)
+    np.testing.assert_allclose(o_m, o_u, atol=1e-13)
+    np.testing.assert_allclose(l_m, l_u, atol=1e-13)
+
+
+def test_merge_special_cases():
+    rng = np.random.default_rng(9)
+    o_a = rng.standard_normal((4, 2, 3))
+    o_b = rng.standard_normal((4, 2, 3))
+    l_a = rng.standard_normal((2, 4))
+    # an empty side contributes nothing
+    o, l = oracle.merge(o_a, l_a, o_b, np.full((2, 4), -np.inf))
+    np.testing.assert_array_equal(o, o_a)
+    np.testing.assert_array_equal(l, l_a)
+    # equal partition sums: the plain mean, LSE + ln 2
+    o, l = oracle.merge(o_a, l_a, o_b, l_a)
+    np.testing.assert_allclose(o, 0.5 * (o_a + o_b), atol=1e-15)
+    np.testing.assert_allclose(l, l_a + math.log(2.0), atol=1e-15)
+    # two empty sides: zero output, -inf
+    o, l = oracle.merge(o_a, np.full((2, 4), -np.inf), o_b, np.full((2, 4), -np.inf))
+    assert np.all(o == 0.0) and np.all(np.isneginf(l))
+
+
+def test_qk_oracle_rejects_mismatched_tables():
+    q = np.zeros((4, 1, 2))
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd_qk(q, q, q, np.array([0, 4], np.int32), np.array([0, 2, 4], np.int32), 1.0)
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd_qk(q, q[:3], q[:3], np.array([0, 4], np.int32), np.array([0, 4], np.int32), 1.0)
