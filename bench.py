@@ -12,6 +12,8 @@ the kernel is launched on) and the fp64 oracle timed on the host's cores on a bo
 row sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C3] [--no-cpu-baseline]
+    python bench.py --config X1          # separate q/k tables: long-Q, short-KV cross-attention
+    python bench.py --op merge           # (O, LSE) merge of two results, C3's shape
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -107,12 +109,145 @@ def cpu_baseline(wl, out_bits, lse, budget_s: float):
     return base, parity
 
 
+PEAK_HBM_GBS = 8000.0                # MI355X HBM3E (published)
+
+
+def timed(step, stream, steps, warmup):
+    """W untimed steps, then K timed steps bracketed by synchronisation; returns (wall ms per
+    step, kernel ms per step from HIP events recorded on the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def bench_cross(args):
+    """Separate query / key tables on a long-Q, short-KV pack: HBM is the roof."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import pfa_varlen_fwd_qk
+    x = W.generate_cross(args.config, seed=args.seed)
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(x.q), up(x.k), up(x.v)
+    cq = torch.from_numpy(x.cu_q).to(dev)
+    ck = torch.from_numpy(x.cu_k).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((x.heads, x.total_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, x.max_k, x.scale, out=out, lse=lse, stream=stream)
+
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    alg = x.total_q * x.heads * (4 * x.head_dim + 4) + x.total_k * x.heads * 4 * x.head_dim
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(1234)
+        rows = np.sort(rng.choice(x.total_q, size=min(x.total_q, 4096), replace=False))
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.varlen_fwd_qk(x.q, x.k, x.v, x.cu_q, x.cu_k, x.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        seg = np.searchsorted(x.cu_q[1:], rows, side="right")
+        flop = 4.0 * float(np.asarray(x.lengths_k)[seg].sum()) * x.heads * x.head_dim
+        o = W.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        d = np.abs(o - o_ref)
+        parity = {"rows": int(len(rows)), "max_abs_err": float(d.max()),
+                  "rel_rms": float(np.sqrt((d * d).sum() / (o_ref * o_ref).sum())),
+                  "lse_max_abs_err": float(np.abs(lse.cpu().numpy()[:, rows] - l_ref).max())}
+        cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"{len(rows)} query rows of {x.name} (all heads), "
+                                           f"{flop / 1e9:.1f} GFLOP of fp64 work in {dt:.1f} s"}
+    rec = {"metric": "cross-attention TFLOP/s (4·ΣLq·Lk·H·d), separate q/k tables, 1 GPU",
+           "value": round(x.flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V; no dataset or weights)",
+           "config": {"workload": f"{x.name}: {W.CROSS_CONFIGS[x.name]['description']}",
+                      "segments_q": list(x.lengths_q), "segments_k": list(x.lengths_k),
+                      "heads": x.heads, "head_dim": x.head_dim, "flop_per_step": x.flops,
+                      "algorithmic_bytes_per_step": alg, "seed": args.seed},
+           "roofline": {"bound": "hbm", "achieved": round(alg / (kms * 1e-3) / 1e9, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5)},
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
+def bench_merge(args):
+    """(O, LSE) merge of two bf16 results at the Mage-Flow pack's shape: HBM-bound."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import pfa_attn_merge
+    c = W.CONFIGS["C3"]
+    T, H, d = sum(c.lengths), c.heads, c.head_dim
+    rng = np.random.default_rng(args.seed)
+    o_a = W.bf16_bits(rng.standard_normal((T, H, d), dtype=np.float32))
+    o_b = W.bf16_bits(rng.standard_normal((T, H, d), dtype=np.float32))
+    l_a = (rng.standard_normal((H, T)) * 4).astype(np.float32)
+    l_b = (rng.standard_normal((H, T)) * 4).astype(np.float32)
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    oa, ob = up(o_a), up(o_b)
+    la, lb = torch.from_numpy(l_a).to(dev), torch.from_numpy(l_b).to(dev)
+    out = torch.empty_like(oa)
+    lse = torch.empty_like(la)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pfa_attn_merge(oa, la, ob, lb, out=out, lse=lse, stream=stream)
+
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    alg = T * H * (3 * 2 * d + 3 * 4)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        fa, fb = W.bf16_to_f64(o_a), W.bf16_to_f64(o_b)
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.merge(fa, l_a.astype(np.float64), fb, l_b.astype(np.float64))
+        dt = time.perf_counter() - t0
+        o = W.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+        # bound: one bf16 rounding of the result (half the spacing at |ref|) plus fp32
+        # arithmetic on the two weighted terms
+        half = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))).astype(np.int64) - 8)
+        bound = half + 2.0 ** -20 * (np.abs(fa) + np.abs(fb))
+        parity = {"max_abs_err": float(np.abs(o - o_ref).max()),
+                  "max_err_over_rounding_bound": float((np.abs(o - o_ref) / bound).max()),
+                  "lse_max_abs_err": float(np.abs(lse.cpu().numpy() - l_ref).max())}
+        cpu = {"value": alg / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole merge (numpy fp64) in {dt:.2f} s"}
+    rec = {"metric": "(O, LSE) merge GB/s (algorithmic bytes T·H·(6d+12)), 1 GPU",
+           "value": round(alg / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded N(0,1) bf16 partial outputs, N(0,16) fp32 LSE)",
+           "config": {"workload": f"merge of two [T={T}, H={H}, d={d}] results",
+                      "algorithmic_bytes_per_step": alg, "seed": args.seed},
+           "roofline": {"bound": "hbm", "achieved": round(alg / (kms * 1e-3) / 1e9, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(alg / (kms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5)},
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS))
+    ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
+    ap.add_argument("--op", default="fwd", choices=["fwd", "merge"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -128,6 +263,12 @@ def main():
     import torch
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.op == "merge":
+        bench_merge(args)
+        return
+    if args.config in W.CROSS_CONFIGS:
+        bench_cross(args)
         return
 
     from packed_varlen_flash_amd import pfa_varlen_fwd

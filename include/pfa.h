@@ -84,6 +84,58 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
                            void* out, float* lse, hipStream_t stream);
 
 /*
+ * pfa_varlen_fwd_qk -- the same forward with separate query and key segment tables.
+ *
+ * The varlen call of the Mage-Flow packed_attention listing takes cu_seqlens_q and
+ * cu_seqlens_k (and max_seqlen_q / max_seqlen_k) as separate arguments; pfa_varlen_fwd
+ * is the case where both are one table.  With different tables, the queries of segment s
+ * are rows [cu_seqlens_q[s], cu_seqlens_q[s+1]) of q and attend exactly the keys
+ * [cu_seqlens_k[s], cu_seqlens_k[s+1]) of k and v: the cross-attention of the xxmr.cn
+ * editing-network article (section 3.1: queries from the draft features, keys and values
+ * from the condition or edit sequence; section 4.1: those sequences are much shorter than
+ * the query sequence).
+ *
+ * q, out        bf16 [Tq, heads, head_dim], Tq = cu_seqlens_q[num_seqs].
+ * k, v          bf16 [Tk, heads, head_dim], Tk = cu_seqlens_k[num_seqs].
+ * cu_seqlens_q, cu_seqlens_k   device int32 [num_seqs + 1]; passing the same pointer for
+ *               both selects the self-attention kernel.
+ * max_seqlen_q  bound on every query segment length (>= 1); sizes the launch.
+ * max_seqlen_k  bound on every key segment length (>= 1); not used by the kernel.
+ * lse           fp32 [heads, Tq] or NULL.
+ * Everything else, ownership and errors as for pfa_varlen_fwd.  A segment with queries
+ * but no keys has no softmax; its rows get O = 0 and LSE = -inf.  Both tables must
+ * satisfy the preconditions of pfa_varlen_fwd (check each with pfa_check_cu_seqlens).
+ */
+PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int num_seqs, int max_seqlen_q, int max_seqlen_k, int heads,
+                              int head_dim, float scale, void* out, float* lse,
+                              hipStream_t stream);
+
+/*
+ * pfa_attn_merge -- combine two results for the same queries over disjoint key sets.
+ *
+ * If (o_a, lse_a) is attention over key set A and (o_b, lse_b) over key set B, the
+ * attention over A and B together has partition sum exp(lse_a) + exp(lse_b) and output
+ *     out = (exp(lse_a) o_a + exp(lse_b) o_b) / (exp(lse_a) + exp(lse_b)),
+ *     lse = ln(exp(lse_a) + exp(lse_b)),
+ * the identity behind the blocked running-max / normaliser update of the GigaPath-Flash
+ * page (section 3.2), applied to two finished blocks.  It joins per-block results of
+ * pfa_varlen_fwd_qk (e.g. key sets split across devices or passes).  A side with
+ * lse = -inf (no keys) contributes nothing; two such sides give out = 0, lse = -inf.
+ *
+ * o_a, o_b, out  device bf16 [total, heads, head_dim]; out may be o_a or o_b (in place).
+ * lse_a, lse_b   device fp32 [heads, total]; lse may be lse_a or lse_b, or NULL.
+ * total          rows (>= 0; 0 does nothing).
+ * Arithmetic in fp32, output rounded to nearest even.  Returns PFA_OK, PFA_ERR_NULL,
+ * PFA_ERR_SIZE, PFA_ERR_HEADS, PFA_ERR_HEAD_DIM (64 or 128), PFA_ERR_ALIAS (an O buffer
+ * shared with an LSE buffer) or PFA_ERR_LAUNCH.  Enqueued on stream; returns at once.
+ */
+PFA_API int pfa_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
+                           const float* lse_b, int64_t total, int heads, int head_dim,
+                           void* out, float* lse, hipStream_t stream);
+
+/*
  * pfa_check_cu_seqlens -- host-side validator of a cu_seqlens table (no device calls).
  *
  * cu_host     host pointer to num_seqs + 1 int32 values.

@@ -14,8 +14,8 @@ import numpy as np
 
 from . import _lib
 
-__all__ = ["pfa_varlen_fwd", "pfa_check_cu_seqlens", "pfa_status_string", "PfaError",
-           "LIB_PATH"]
+__all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_attn_merge", "pfa_check_cu_seqlens",
+           "pfa_status_string", "PfaError", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
 
@@ -39,6 +39,20 @@ def pfa_check_cu_seqlens(cu_host, max_seqlen: int) -> int:
     if rc != 0:
         raise PfaError(rc)
     return int(total.value)
+
+
+def _check_bf16(name, t, torch):
+    if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 3:
+        raise ValueError(f"{name} must be a contiguous bf16 CUDA tensor [T, H, d]")
+
+
+def _check_table(name, cu, torch):
+    if not cu.is_cuda or cu.dtype != torch.int32 or not cu.is_contiguous() or cu.dim() != 1:
+        raise ValueError(f"{name} must be a contiguous 1-D int32 CUDA tensor")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
 def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None,
@@ -78,6 +92,74 @@ def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
         float(scale), ctypes.c_void_p(out.data_ptr()),
         ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
         ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse
+
+
+def pfa_varlen_fwd_qk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                      scale: float | None = None, out=None, lse=None, want_lse: bool = True,
+                      stream=None):
+    """Forward with separate query and key segment tables (queries of segment s attend
+    the keys of segment s).  q: [Tq, H, d]; k, v: [Tk, H, d]; cu tables int32 [n + 1].
+    Returns (out [Tq, H, d] bf16, lse [H, Tq] fp32 or None)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t, torch)
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [Tk, H, d] with q's H and d")
+    _check_table("cu_seqlens_q", cu_seqlens_q, torch)
+    _check_table("cu_seqlens_k", cu_seqlens_k, torch)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    Tq, H, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (H, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [H, Tq]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_fwd_qk(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        cu_seqlens_q.numel() - 1, int(max_seqlen_q), int(max_seqlen_k), H, d, float(scale),
+        _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse
+
+
+def pfa_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, want_lse: bool = True,
+                   stream=None):
+    """Combine two results for the same queries over disjoint key sets (see pfa.h).
+    o_*: bf16 [T, H, d]; lse_*: fp32 [H, T].  out / lse may be o_a / lse_a (in place).
+    Returns (out, lse or None)."""
+    import torch
+
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        _check_bf16(name, t, torch)
+    if o_b.shape != o_a.shape:
+        raise ValueError("o_a and o_b must have the same shape")
+    T, H, d = o_a.shape
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t.shape != (H, T) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor [H, T]")
+    if out is None:
+        out = torch.empty_like(o_a)
+    elif out.shape != o_a.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like o_a")
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=o_a.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_a.device)
+    rc = _lib.load().pfa_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), T, H, d,
+                                    _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise PfaError(rc)
     return out, lse

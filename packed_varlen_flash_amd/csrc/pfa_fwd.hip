@@ -65,7 +65,8 @@ struct Params {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
-  const int32_t* cu;
+  const int32_t* cu_q;   // query segment table
+  const int32_t* cu_k;   // key / value segment table (the same pointer for self-attention)
   __bf16* out;
   float* lse;
   int num_seqs;
@@ -132,15 +133,17 @@ __device__ __forceinline__ float partner_sum(float x) {
 // ---------------------------------------------------------------------------------
 // Device-side scheduler: decode cu_seqlens into a longest-first list of work items.
 // ---------------------------------------------------------------------------------
-// Sorted mode (num_seqs <= kSortMax): s_order[r] = segment of rank r (length
-// descending, ties by index), s_prefix[r] = first item of rank r; items of one segment
-// are ordered head-major, query-tile-minor.  Returns the item count.
+// Sorted mode (num_seqs <= kSortMax): s_order[r] = segment of rank r (key length, i.e.
+// the work per query tile, descending; ties by index), s_prefix[r] = first item of rank
+// r; a segment has heads * ceil(query length / BM) items, ordered head-major,
+// query-tile-minor.  Returns the item count.
 template <int BM, int THREADS>
-__device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_prefix) {
+__device__ int build_schedule(const Params& p, const int32_t* cu_k, int* s_len, int* s_order,
+                              int* s_prefix) {
   const int n = p.num_seqs;
   const int tid = threadIdx.x;
   for (int s = tid; s < n; s += THREADS) {
-    int L = p.cu[s + 1] - p.cu[s];
+    int L = cu_k[s + 1] - cu_k[s];
     s_len[s] = L > 0 ? L : 0;
   }
   __syncthreads();
@@ -156,8 +159,10 @@ __device__ int build_schedule(const Params& p, int* s_len, int* s_order, int* s_
   __syncthreads();
   // items per rank, then an inclusive Hillis-Steele scan in place (n <= kSortMax)
   for (int r = tid; r < n; r += THREADS) {
-    const int L = s_len[s_order[r]];
-    s_prefix[r + 1] = p.heads * ((L + BM - 1) / BM);
+    const int sg = s_order[r];
+    int Lq = p.cu_q[sg + 1] - p.cu_q[sg];
+    Lq = Lq > 0 ? Lq : 0;
+    s_prefix[r + 1] = p.heads * ((Lq + BM - 1) / BM);
   }
   if (tid == 0) s_prefix[0] = 0;
   __syncthreads();
@@ -301,8 +306,8 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
 }
 
 // Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
-// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of rounded weights can
-// carry up to 2^-9 relative error into the LSE of a sharp row).  l_rnd adds the bf16
+// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of bf16-rounded weights
+// can carry up to 2^-8 relative error, 3.9e-3, into the LSE of a sharp row).  l_rnd adds the bf16
 // weights the PV product actually uses and normalises O: the rounding of each weight then
 // enters numerator and denominator alike, which measurably tightens the worst output error
 // on sharp rows.  Both sums chain straight into their running values (one add, resp. one
@@ -376,9 +381,11 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
   }
 }
 
-template <int D, int QB, int NW, int SK>
-__device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int seg_a,
-                                             int L, int h, int qt, int T) {
+// CROSS only keys the instantiation to its kernel variant (the HIP host pass rejects a
+// device template specialisation shared by two kernel templates' instantiations).
+template <int D, int QB, int NW, int SK, bool CROSS>
+__device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int qa,
+                                             int Lq, int ka, int Lk, int h, int qt, int Tq) {
   using C = Tile<D, QB, NW, SK>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -389,11 +396,11 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const int hh = (lane >> 4) & 1;
   const int64_t rs = (int64_t)p.heads * D;  // elements between consecutive tokens
   const int64_t head_off = (int64_t)h * D;
-  const __bf16* qbase = p.q + (int64_t)seg_a * rs + head_off;
-  const __bf16* kbase = p.k + (int64_t)seg_a * rs + head_off;
-  const __bf16* vbase = p.v + (int64_t)seg_a * rs + head_off;
+  const __bf16* qbase = p.q + (int64_t)qa * rs + head_off;
+  const __bf16* kbase = p.k + (int64_t)ka * rs + head_off;
+  const __bf16* vbase = p.v + (int64_t)ka * rs + head_off;
   const int q0 = qt * C::BM + wave * (QB * 32);
-  const int ns = (L + SK - 1) / SK;        // LDS stages
+  const int ns = (Lk + SK - 1) / SK;       // LDS stages (0 when the key segment is empty)
   const float c = p.c;
 
   TileState<D, QB> st;
@@ -403,7 +410,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
     for (int t = 0; t < C::KSTEP; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < L) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * rs + 16 * t + 8 * g);
+      if (row < Lq) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * rs + 16 * t + 8 * g);
       st.qr[b][t] = __builtin_bit_cast(bf16x8, x);
     }
     st.m_run[b] = -INFINITY;
@@ -439,7 +446,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
     const int kb = stage * SK;
-    const int rows = (L - kb < SK) ? (L - kb) : SK;
+    const int rows = (Lk - kb < SK) ? (Lk - kb) : SK;
     const int nrec = rows * row_bytes;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
@@ -458,17 +465,19 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   // right after the barrier that retires every reader of its slot, and have the whole of
   // stage s to land.  Unrolled by two so both slot offsets are immediates.
   static_assert(kStages == 2, "the stage loop alternates two slots");
-  issue_fn(kring, vring, 0);
+  // no keys, no loads: a zero-row stage would still zero-fill slot 0, which the epilogue
+  // reuses for the output
+  if (ns > 0) issue_fn(kring, vring, 0);
   for (int s = 0; s < ns; s += 2) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
     stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
-                      issue_fn, s, L, koff, voff, c, g);
+                      issue_fn, s, Lk, koff, voff, c, g);
     if (s + 1 >= ns) break;
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
     stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
-                      issue_fn, s + 1, L, koff, voff, c, g);
+                      issue_fn, s + 1, Lk, koff, voff, c, g);
   }
   __syncthreads();   // every wave has left the ring
 
@@ -482,7 +491,8 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = partner_sum(st.l_run[b]);
-    const float inv = 1.0f / partner_sum(st.l_rnd[b]);
+    const float lr = partner_sum(st.l_rnd[b]);
+    const float inv = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
     const int r = b * 32 + n32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -493,8 +503,8 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
         for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv);
         *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(r, 4 * dt + ii) + 8 * g) = w;
       }
-    if (p.lse != nullptr && g == 0 && q0 + r < L)
-      p.lse[(int64_t)h * T + seg_a + q0 + r] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
+    if (p.lse != nullptr && g == 0 && q0 + r < Lq)
+      p.lse[(int64_t)h * Tq + qa + q0 + r] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
   }
   __syncthreads();
   constexpr int OCH = QB * 32 * C::CPR;      // 16-byte chunks of the wave's block
@@ -505,15 +515,18 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     const int r = P / C::CPR;
     const int ch = P % C::CPR;
     const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, true>(r, ch));
-    if (q0 + r < L)
-      *reinterpret_cast<u32x4*>(p.out + (int64_t)(seg_a + q0 + r) * rs + head_off + ch * 8) = x;
+    if (q0 + r < Lq)
+      *reinterpret_cast<u32x4*>(p.out + (int64_t)(qa + q0 + r) * rs + head_off + ch * 8) = x;
   }
   __syncthreads();   // the next tile's first stage overwrites the ring
 }
 
-template <int D, int QB, int NW, int SK, int WPE>
+// CROSS: separate query and key tables; otherwise the key table is the query table
+// (known at compile time, so the key-side offsets and lengths fold into the query ones).
+template <int D, int QB, int NW, int SK, int WPE, bool CROSS>
 __global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 pfa_fwd_kernel(Params p) {
+  const int32_t* const cu_k = CROSS ? p.cu_k : p.cu_q;
   using C = Tile<D, QB, NW, SK>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
@@ -522,11 +535,12 @@ pfa_fwd_kernel(Params p) {
   int* s_prefix = s_order + kSortMax;
   int* s_len = reinterpret_cast<int*>(ks);  // scratch, dead before the first K tile lands
 
-  const int T = p.cu[p.num_seqs];
+  const int Tq = p.cu_q[p.num_seqs];
+  const int Tk = cu_k[p.num_seqs];
   const bool sorted = p.num_seqs <= kSortMax;
   int total;
   if (sorted) {
-    total = build_schedule<C::BM, C::THREADS>(p, s_len, s_order, s_prefix);
+    total = build_schedule<C::BM, C::THREADS>(p, cu_k, s_len, s_order, s_prefix);
   } else {
     total = p.num_seqs * p.heads * p.qt_max;
   }
@@ -540,7 +554,7 @@ pfa_fwd_kernel(Params p) {
   for (int base = 0; base < total; base += G) {
     const int u = base + slot;
     if (u >= total) break;
-    int s, h, qt, a, L;
+    int s, h, qt;
     if (sorted) {
       int lo = 0, hi = p.num_seqs - 1;   // last rank r with s_prefix[r] <= u
       while (lo < hi) {
@@ -548,9 +562,7 @@ pfa_fwd_kernel(Params p) {
         if (s_prefix[mid] <= u) lo = mid; else hi = mid - 1;
       }
       s = s_order[lo];
-      a = p.cu[s];
-      L = p.cu[s + 1] - a;
-      const int ntiles = (L + C::BM - 1) / C::BM;
+      const int ntiles = (p.cu_q[s + 1] - p.cu_q[s] + C::BM - 1) / C::BM;
       const int local = u - s_prefix[lo];
       h = local / ntiles;
       qt = local - h * ntiles;
@@ -560,15 +572,76 @@ pfa_fwd_kernel(Params p) {
       const int rem = u - s * per_seg;
       h = rem / p.qt_max;
       qt = rem - h * p.qt_max;
-      a = p.cu[s];
-      L = p.cu[s + 1] - a;
     }
-    // never touch rows outside [0, T), whatever the table says
-    if (a < 0 || a >= T) continue;
-    if (L > T - a) L = T - a;
-    if (L <= 0 || qt * C::BM >= L) continue;
-    process_tile<D, QB, NW, SK>(p, ks, vs, a, L, h, qt, T);
+    const int qa = p.cu_q[s];
+    int Lq = p.cu_q[s + 1] - qa;
+    // never touch rows outside [0, Tq) / [0, Tk), whatever the tables say
+    if (qa < 0 || qa >= Tq) continue;
+    if (Lq > Tq - qa) Lq = Tq - qa;
+    if (Lq <= 0 || qt * C::BM >= Lq) continue;
+    int ka = qa, Lk = Lq;
+    if (CROSS) {
+      ka = cu_k[s];
+      Lk = cu_k[s + 1] - ka;
+      if (ka < 0 || ka > Tk) ka = Tk;
+      if (Lk > Tk - ka) Lk = Tk - ka;
+      if (Lk < 0) Lk = 0;
+    }
+    process_tile<D, QB, NW, SK, CROSS>(p, ks, vs, qa, Lq, ka, Lk, h, qt, Tq);
   }
+}
+
+// ---------------------------------------------------------------------------------
+// (O, LSE) merge of two results for the same queries over disjoint key sets A and B.
+// With Z_X = exp(LSE_X) the partition sum over X, the union has Z_A + Z_B and its output
+// is the Z-weighted mean of O_A and O_B: the identity behind the blocked update of the
+// GigaPath-Flash page (section 3.2), applied to two finished blocks.  One thread per
+// 16-byte chunk (8 values) of one (token, head) row; a row's chunks are consecutive
+// lanes of one wave, so every lane has read its row's LSE values before any lane
+// stores, and the result may overwrite either input in place.  HBM-bound.
+// ---------------------------------------------------------------------------------
+constexpr int kMergeThreads = 256;
+
+struct MergeParams {
+  const __bf16* o_a;
+  const __bf16* o_b;
+  const float* lse_a;
+  const float* lse_b;
+  __bf16* out;
+  float* lse;
+  int64_t total;
+  int heads;
+  int cpr;   // 16-byte chunks per row (head_dim / 8)
+};
+
+__global__ void __launch_bounds__(kMergeThreads) pfa_merge_kernel(MergeParams m) {
+  const int64_t idx = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+  const int64_t row = idx / m.cpr;             // (token, head) row, head fastest
+  const int ch = (int)(idx - row * m.cpr);
+  if (row >= m.total * m.heads) return;
+  const int64_t t = row / m.heads;
+  const int h = (int)(row - t * m.heads);
+  const float la = m.lse_a[(int64_t)h * m.total + t];
+  const float lb = m.lse_b[(int64_t)h * m.total + t];
+  const float mx = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f, l = -INFINITY;
+  if (mx != -INFINITY) {                        // at least one side has keys
+    wa = __builtin_amdgcn_exp2f((la - mx) * kLog2e);
+    wb = __builtin_amdgcn_exp2f((lb - mx) * kLog2e);
+    const float z = wa + wb;
+    l = mx + __builtin_amdgcn_logf(z) * kLn2;
+    const float inv = 1.0f / z;
+    wa *= inv;
+    wb *= inv;
+  }
+  const int64_t off = row * (int64_t)(m.cpr * 8) + ch * 8;
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(m.o_a + off);
+  const bf16x8 b = *reinterpret_cast<const bf16x8*>(m.o_b + off);
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)(wa * (float)a[e] + wb * (float)b[e]);
+  *reinterpret_cast<bf16x8*>(m.out + off) = r;
+  if (m.lse != nullptr && ch == 0) m.lse[(int64_t)h * m.total + t] = l;
 }
 
 // ---------------------------------------------------------------------------------
@@ -581,19 +654,19 @@ struct Variant {
   size_t lds;
 };
 
-template <int D, int QB, int NW, int SK, int WPE>
+template <int D, int QB, int NW, int SK, int WPE, bool CROSS>
 Variant make_variant() {
   using C = Tile<D, QB, NW, SK>;
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE>), C::BM,
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, CROSS>), C::BM,
                  C::THREADS, C::LDS_BYTES};
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 2;  // head_dim 64, 128
+constexpr int kVariants = 4;  // head_dim 64, 128; one table or separate q / k tables
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 
-int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
+int variant_index(int head_dim, bool cross) { return (head_dim == 64 ? 0 : 1) + (cross ? 2 : 0); }
 
 #ifndef PFA_D64_QB
 #define PFA_D64_QB 2
@@ -620,9 +693,12 @@ int variant_index(int head_dim) { return head_dim == 64 ? 0 : 1; }
 #define PFA_D128_SK 64
 #endif
 
-Variant variant_for(int head_dim) {
-  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE>();
-  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE>();
+Variant variant_for(int head_dim, bool cross) {
+  if (head_dim == 64)
+    return cross ? make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, true>()
+                 : make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, false>();
+  return cross ? make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, true>()
+               : make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, false>();
 }
 
 }  // namespace
@@ -661,23 +737,26 @@ PFA_API int pfa_check_cu_seqlens(const int32_t* cu_host, int num_seqs, int max_s
   return PFA_OK;
 }
 
-PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
-                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
-                           void* out, float* lse, hipStream_t stream) {
+PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int num_seqs, int max_seqlen_q,
+                              int max_seqlen_k, int heads, int head_dim, float scale, void* out,
+                              float* lse, hipStream_t stream) {
   // ---- argument checks: all before any HIP runtime call
-  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens == nullptr || out == nullptr)
+  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr || out == nullptr)
     return PFA_ERR_NULL;
   if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
   if (heads < 1) return PFA_ERR_HEADS;
-  if (max_seqlen < 1) return PFA_ERR_MAX_SEQLEN;
+  if (max_seqlen_q < 1 || max_seqlen_k < 1) return PFA_ERR_MAX_SEQLEN;
   if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
   if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
-  const void* ins[4] = {q, k, v, cu_seqlens};
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
   for (const void* in : ins)
     if (in == out || (lse != nullptr && in == static_cast<const void*>(lse))) return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
-  const Variant var = variant_for(head_dim);
-  const int64_t qt_max = ((int64_t)max_seqlen + var.bm - 1) / var.bm;
+  const bool cross = cu_seqlens_k != cu_seqlens_q;
+  const Variant var = variant_for(head_dim, cross);
+  const int64_t qt_max = ((int64_t)max_seqlen_q + var.bm - 1) / var.bm;
   const int64_t slots = (int64_t)num_seqs * heads * qt_max;
   if ((int64_t)heads * head_dim > INT32_MAX || slots > INT32_MAX) return PFA_ERR_SIZE;
 
@@ -690,7 +769,7 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
       return PFA_ERR_DEVICE;
     g_cus[dev].store(cus, std::memory_order_relaxed);
   }
-  const int vi = variant_index(head_dim);
+  const int vi = variant_index(head_dim, cross);
   int occ = g_occ[dev][vi].load(std::memory_order_relaxed);
   if (occ <= 0) {
     if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)var.lds) != hipSuccess)
@@ -710,7 +789,8 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
   prm.q = static_cast<const __bf16*>(q);
   prm.k = static_cast<const __bf16*>(k);
   prm.v = static_cast<const __bf16*>(v);
-  prm.cu = cu_seqlens;
+  prm.cu_q = cu_seqlens_q;
+  prm.cu_k = cu_seqlens_k;
   prm.out = static_cast<__bf16*>(out);
   prm.lse = lse;
   prm.num_seqs = num_seqs;
@@ -719,6 +799,47 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
   prm.c = scale * kLog2e;
   void* args[] = {&prm};
   const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, var.lds, stream);
+  return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
+}
+
+PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
+                           void* out, float* lse, hipStream_t stream) {
+  return pfa_varlen_fwd_qk(q, k, v, cu_seqlens, cu_seqlens, num_seqs, max_seqlen, max_seqlen, heads,
+                           head_dim, scale, out, lse, stream);
+}
+
+PFA_API int pfa_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                           int64_t total, int heads, int head_dim, void* out, float* lse,
+                           hipStream_t stream) {
+  if (o_a == nullptr || lse_a == nullptr || o_b == nullptr || lse_b == nullptr || out == nullptr)
+    return PFA_ERR_NULL;
+  if (total < 0) return PFA_ERR_SIZE;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  const void* ins[4] = {o_a, lse_a, o_b, lse_b};
+  for (const void* in : ins)   // in place on one side is allowed; crossing o and lse is not
+    if ((lse != nullptr && static_cast<const void*>(lse) == out) ||
+        (in == static_cast<const void*>(out) && (in == lse_a || in == lse_b)) ||
+        (lse != nullptr && in == static_cast<const void*>(lse) && (in == o_a || in == o_b)))
+      return PFA_ERR_ALIAS;
+  if (total == 0) return PFA_OK;
+  const int64_t chunks = total * heads * (head_dim / 8);
+  const int64_t blocks = (chunks + kMergeThreads - 1) / kMergeThreads;
+  if (total > INT32_MAX || blocks > INT32_MAX) return PFA_ERR_SIZE;
+  MergeParams mp;
+  mp.o_a = static_cast<const __bf16*>(o_a);
+  mp.o_b = static_cast<const __bf16*>(o_b);
+  mp.lse_a = lse_a;
+  mp.lse_b = lse_b;
+  mp.out = static_cast<__bf16*>(out);
+  mp.lse = lse;
+  mp.total = total;
+  mp.heads = heads;
+  mp.cpr = head_dim / 8;
+  void* args[] = {&mp};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&pfa_merge_kernel),
+                                         dim3((unsigned)blocks), dim3(kMergeThreads), args, 0, stream);
   return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 

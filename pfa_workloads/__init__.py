@@ -145,6 +145,84 @@ def generate(name: str, seed: int = 0) -> Workload:
                 per_head_qk_scale=c.per_head_qk_scale)
 
 
+@dataclasses.dataclass
+class CrossWorkload:
+    """Separate query and key segment tables: queries of segment s attend keys of s."""
+    name: str
+    q: np.ndarray          # uint16 bf16 bits [Tq, H, d]
+    k: np.ndarray          # [Tk, H, d]
+    v: np.ndarray          # [Tk, H, d]
+    cu_q: np.ndarray       # int32 [num_seqs + 1]
+    cu_k: np.ndarray
+    lengths_q: tuple
+    lengths_k: tuple
+    heads: int
+    head_dim: int
+    scale: float
+    seed: int
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_q[-1])
+
+    @property
+    def total_k(self) -> int:
+        return int(self.cu_k[-1])
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.lengths_q)
+
+    @property
+    def max_q(self) -> int:
+        return max(max(self.lengths_q), 1)
+
+    @property
+    def max_k(self) -> int:
+        return max(max(self.lengths_k), 1)
+
+    @property
+    def flops(self) -> float:
+        return 4.0 * float(sum(int(a) * int(b) for a, b in zip(self.lengths_q, self.lengths_k))) \
+            * self.heads * self.head_dim
+
+
+def make_cross(lengths_q, lengths_k, heads: int, head_dim: int, seed: int = 0,
+               name: str = "cross", scale: float | None = None) -> CrossWorkload:
+    """Draw Q [Tq, H, d], then K and V [Tk, H, d], N(0,1) float32, rounded to bf16."""
+    lengths_q = tuple(int(L) for L in lengths_q)
+    lengths_k = tuple(int(L) for L in lengths_k)
+    if len(lengths_q) != len(lengths_k):
+        raise ValueError("one key length per query segment")
+    rng = np.random.default_rng(seed)
+    tq, tk = int(sum(lengths_q)), int(sum(lengths_k))
+    q = rng.standard_normal((tq, heads, head_dim), dtype=np.float32)
+    k = rng.standard_normal((tk, heads, head_dim), dtype=np.float32)
+    v = rng.standard_normal((tk, heads, head_dim), dtype=np.float32)
+    return CrossWorkload(name=name, q=bf16_bits(q), k=bf16_bits(k), v=bf16_bits(v),
+                         cu_q=cu_from_lengths(lengths_q), cu_k=cu_from_lengths(lengths_k),
+                         lengths_q=lengths_q, lengths_k=lengths_k, heads=heads,
+                         head_dim=head_dim,
+                         scale=float(scale) if scale is not None else 1.0 / math.sqrt(head_dim),
+                         seed=seed)
+
+
+# Cross-attention workload: the Mage-Flow mixed pack's image tokens (C3's segments, same
+# order) as queries, each image attending its own 256-token condition sequence ("long Q,
+# short KV").  The pages give no condition length; 256 is the reading used here.
+CROSS_CONFIGS = {
+    "X1": dict(lengths_q=tuple(_c3_lengths()), lengths_k=(256,) * 16, heads=24, head_dim=128,
+               description="cross-attention: 16 images (7x4096+5x1296+4x1024 query tokens) "
+                           "each attending 256 condition tokens, 24 heads, head_dim 128"),
+}
+
+
+def generate_cross(name: str, seed: int = 0) -> CrossWorkload:
+    c = CROSS_CONFIGS[name]
+    return make_cross(c["lengths_q"], c["lengths_k"], c["heads"], c["head_dim"], seed=seed,
+                      name=name)
+
+
 def sample_rows(cu_seqlens, stride: int = 61, edge: int = 128, full_upto: int = 4096) -> np.ndarray:
     """Deterministic row sample for configurations too large for the oracle in full.
 

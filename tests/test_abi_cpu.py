@@ -26,7 +26,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_check_cu_seqlens", "pfa_status_string"}
+    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_attn_merge",
+                                       "pfa_check_cu_seqlens", "pfa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -63,6 +64,45 @@ def test_argument_checks_run_before_any_hip_call(lib):
     assert _fwd(lib, lse=2) == -7
     assert _fwd(lib, lse=5) == -7
     assert _fwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
+
+
+def _fwd_qk(lib, q=1, k=2, v=3, cu_q=4, cu_k=8, num_seqs=1, max_q=1, max_k=1, heads=1,
+            head_dim=64, scale=1.0, out=5, lse=6):
+    return lib.pfa_varlen_fwd_qk(q, k, v, cu_q, cu_k, num_seqs, max_q, max_k, heads, head_dim, scale,
+                                 out, lse, None)
+
+
+def test_qk_argument_checks_run_before_any_hip_call(lib):
+    assert _fwd_qk(lib, cu_k=None) == -1
+    assert _fwd_qk(lib, cu_q=None) == -1
+    assert _fwd_qk(lib, num_seqs=0) == -2
+    assert _fwd_qk(lib, heads=0) == -3
+    assert _fwd_qk(lib, max_q=0) == -4
+    assert _fwd_qk(lib, max_k=0) == -4
+    assert _fwd_qk(lib, head_dim=96) == -5
+    assert _fwd_qk(lib, scale=float("nan")) == -6
+    assert _fwd_qk(lib, out=8) == -7      # out aliases the key table
+    assert _fwd_qk(lib, lse=8) == -7
+    assert _fwd_qk(lib, lse=5) == -7
+    assert _fwd_qk(lib, num_seqs=2**30, heads=2**10, max_q=2**20) == -11
+
+
+def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):
+    return lib.pfa_attn_merge(o_a, lse_a, o_b, lse_b, total, heads, head_dim, out, lse, None)
+
+
+def test_merge_argument_checks_run_before_any_hip_call(lib):
+    assert _merge(lib, o_a=None) == -1
+    assert _merge(lib, lse_b=None) == -1
+    assert _merge(lib, out=None) == -1
+    assert _merge(lib, total=-1) == -11
+    assert _merge(lib, heads=0) == -3
+    assert _merge(lib, head_dim=32) == -5
+    assert _merge(lib, out=2, lse=9) == -7     # out is an LSE input
+    assert _merge(lib, out=9, lse=1) == -7     # lse is an O input
+    assert _merge(lib, out=9, lse=9) == -7     # out and lse the same buffer
+    assert _merge(lib, total=0) == 0           # nothing to do, nothing launched
+    assert _merge(lib, total=2**31, heads=1) == -11
 
 
 def test_host_validator(lib):
