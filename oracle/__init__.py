@@ -15,6 +15,8 @@ marshals:
   queries but no keys gives a zero output and ``lse = -inf``.
 * ``merge(o_a, lse_a, o_b, lse_b)`` -> ``(o, lse)``: attention over the union of two
   disjoint key sets from the results over each (fp64, see its docstring).
+* ``varlen_bwd(q, k, v, dout, cu_seqlens, scale)`` -> ``(dq, dk, dv)`` fp64 ``[T, H, d]``:
+  the gradients of the self-attention forward for upstream gradient ``dout``.
 * ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
   probability matrix over all ``T`` tokens (zero off-segment).
 
@@ -62,6 +64,8 @@ def _load():
         lib.pfa_oracle_fwd_qk.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f64, vp, i64,
                                           vp, vp]
         lib.pfa_oracle_fwd_qk.restype = i32
+        lib.pfa_oracle_bwd.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, i32, f64, vp, vp, vp]
+        lib.pfa_oracle_bwd.restype = i32
         lib.pfa_oracle_probs.argtypes = [i32, vp, vp, vp, i32, i32, i32, f64, i64, i32, vp]
         lib.pfa_oracle_probs.restype = i32
         lib.pfa_oracle_num_threads.argtypes = []
@@ -146,6 +150,25 @@ def varlen_fwd_qk(q, k, v, cu_q, cu_k, scale: float, rows=None):
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return out, lse
+
+
+def varlen_bwd(q, k, v, dout, cu_seqlens, scale: float):
+    q, k, v, dout = (np.ascontiguousarray(a) for a in (q, k, v, dout))
+    kind = _kind(q)
+    if any(_kind(a) != kind for a in (k, v, dout)):
+        raise TypeError("q, k, v and dout must share one element type")
+    if q.ndim != 3 or any(a.shape != q.shape for a in (k, v, dout)):
+        raise ValueError("expected q, k, v, dout all [T, H, d]")
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    T, H, d = q.shape
+    if cu.shape[0] < 2 or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens must have >= 2 entries and end at T")
+    dq, dk, dv = (np.empty((T, H, d), dtype=np.float64) for _ in range(3))
+    rc = _load().pfa_oracle_bwd(kind, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cu),
+                                cu.shape[0] - 1, H, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    return dq, dk, dv
 
 
 def merge(o_a, lse_a, o_b, lse_b):

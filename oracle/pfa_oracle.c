@@ -220,6 +220,89 @@ int pfa_oracle_probs(int kind, const void* q, const void* k, const int32_t* cu, 
   return ORACLE_OK;
 }
 
+/*
+ * Backward of the same definition, for upstream gradient dO of O (one table, as in
+ * self-attention).  The pages train with this path (Mage-Flow page: the packing gains are
+ * training throughput), but print no gradient formulas; these are the plain chain rule of
+ * the forward definition above, written out (fp64, exact input values):
+ *     P_ij  = exp(s_ij - LSE_i)                    (softmax over the segment of i)
+ *     dV_j  = sum_i P_ij dO_i                      (O_i = sum_j P_ij v_j)
+ *     dP_ij = dO_i . v_j
+ *     dS_ij = P_ij (dP_ij - sum_t P_it dP_it)      (softmax Jacobian)
+ *     dQ_i  = scale sum_j dS_ij k_j,   dK_j = scale sum_i dS_ij q_i   (s_ij = scale q_i.k_j)
+ * Rows are processed one query at a time: scores, exact max, normaliser, probabilities,
+ * then dP, the row term sum_t P_it dP_it, dS, and the row's contributions to dQ, dK, dV.
+ * Outputs are fp64 [T, heads, d]; (segment, head) pairs run in parallel, each owning its
+ * key rows of dK / dV.
+ */
+int pfa_oracle_bwd(int kind, const void* q, const void* k, const void* v, const void* dout,
+                   const int32_t* cu, int num_seqs, int heads, int d, double scale, double* dq,
+                   double* dk, double* dv) {
+  if (kind != ELEM_F64 && kind != ELEM_BF16) return ORACLE_EINVAL;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || heads < 1 || d < 1) return ORACLE_EINVAL;
+  if (check_table(cu, num_seqs) != ORACLE_OK) return ORACLE_EINVAL;
+  const int64_t total = cu[num_seqs];
+  const int maxlen = max_segment_length(cu, num_seqs);
+  for (int64_t x = 0; x < total * heads * (int64_t)d; ++x) dq[x] = dk[x] = dv[x] = 0.0;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+    double* dp = (double*)malloc(sizeof(double) * (size_t)(maxlen > 0 ? maxlen : 1));
+    if (!p || !dp) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (int64_t w = 0; w < (int64_t)num_seqs * heads; ++w) {
+        const int s = (int)(w / heads);
+        const int h = (int)(w % heads);
+        const int64_t a = cu[s], b = cu[s + 1];
+        for (int64_t i = a; i < b; ++i) {
+          const int64_t qi = (i * heads + h) * (int64_t)d;
+          /* probabilities of row i (two passes: exact max, then normaliser) */
+          double m = -INFINITY;
+          for (int64_t j = a; j < b; ++j) {
+            const int64_t kj = (j * heads + h) * (int64_t)d;
+            double dot = 0.0;
+            for (int t = 0; t < d; ++t) dot += load_elem(kind, q, qi + t) * load_elem(kind, k, kj + t);
+            p[j - a] = scale * dot;
+            if (p[j - a] > m) m = p[j - a];
+          }
+          double z = 0.0;
+          for (int64_t j = a; j < b; ++j) {
+            p[j - a] = exp(p[j - a] - m);
+            z += p[j - a];
+          }
+          for (int64_t j = a; j < b; ++j) p[j - a] /= z;
+          /* dP_ij = dO_i . v_j and the row term sum_j P_ij dP_ij */
+          double rowterm = 0.0;
+          for (int64_t j = a; j < b; ++j) {
+            const int64_t vj = (j * heads + h) * (int64_t)d;
+            double dot = 0.0;
+            for (int t = 0; t < d; ++t) dot += load_elem(kind, dout, qi + t) * load_elem(kind, v, vj + t);
+            dp[j - a] = dot;
+            rowterm += p[j - a] * dot;
+          }
+          /* dS, then this row's contributions */
+          for (int64_t j = a; j < b; ++j) {
+            const double ds = p[j - a] * (dp[j - a] - rowterm);
+            const int64_t kj = (j * heads + h) * (int64_t)d;
+            for (int t = 0; t < d; ++t) {
+              dq[qi + t] += scale * ds * load_elem(kind, k, kj + t);
+              dk[kj + t] += scale * ds * load_elem(kind, q, qi + t);
+              dv[kj + t] += p[j - a] * load_elem(kind, dout, qi + t);
+            }
+          }
+        }
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  return failed ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
 /* Threads an OpenMP parallel region of the oracle uses (1 without OpenMP). */
 int pfa_oracle_num_threads(void) {
 #ifdef _OPENMP

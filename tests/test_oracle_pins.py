@@ -444,3 +444,89 @@ def test_qk_oracle_rejects_mismatched_tables():
         oracle.varlen_fwd_qk(q, q, q, np.array([0, 4], np.int32), np.array([0, 2, 4], np.int32), 1.0)
     with pytest.raises(ValueError):
         oracle.varlen_fwd_qk(q, q[:3], q[:3], np.array([0, 4], np.int32), np.array([0, 4], np.int32), 1.0)
+
+
+# ---------------------------------------------------------------------------------
+# Backward (dQ, dK, dV for an upstream gradient dO of O).
+# ---------------------------------------------------------------------------------
+
+def _bwd_case(seed, lengths=(5, 1, 0, 9), H=2, d=6):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    return [rng.standard_normal((T, H, d)) for _ in range(4)] + [cu]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_backward_matches_finite_differences_of_the_forward(seed):
+    # f = sum(dO * O(q, k, v)); its directional derivative along a random direction must
+    # equal <grad, direction>.  Central differences of the fp64 forward oracle, step 1e-5:
+    # truncation ~1e-10, cancellation ~1e-11.
+    q, k, v, do, cu = _bwd_case(seed)
+    scale = 0.7
+    dq, dk, dv = oracle.varlen_bwd(q, k, v, do, cu, scale)
+    rng = np.random.default_rng(100 + seed)
+    f = lambda a, b, c: float((oracle.varlen_fwd(a, b, c, cu, scale)[0] * do).sum())
+    eps = 1e-5
+    for which in range(3):
+        dirs = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)]
+        dirs[which] = rng.standard_normal(q.shape)
+        plus = [x + eps * e for x, e in zip((q, k, v), dirs)]
+        minus = [x - eps * e for x, e in zip((q, k, v), dirs)]
+        fd = (f(*plus) - f(*minus)) / (2 * eps)
+        an = float(((dq, dk, dv)[which] * dirs[which]).sum())
+        assert abs(fd - an) <= 1e-7 * (1.0 + abs(an)), (which, fd, an)
+
+
+def test_backward_matches_torch_autograd_fp64():
+    q, k, v, do, cu = _bwd_case(7, lengths=(33, 2, 17), H=3, d=16)
+    scale = 0.25
+    dq, dk, dv = oracle.varlen_bwd(q, k, v, do, cu, scale)
+    for s in range(3):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        tq, tk, tv = (torch.tensor(x[sl].transpose(1, 0, 2), requires_grad=True) for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+        o.backward(torch.tensor(do[sl].transpose(1, 0, 2)))
+        for ours, ref in ((dq, tq), (dk, tk), (dv, tv)):
+            np.testing.assert_allclose(ours[sl], ref.grad.numpy().transpose(1, 0, 2), atol=1e-12)
+
+
+def test_backward_closed_forms():
+    # length 1: the softmax weight is 1 whatever the score, so dQ = dK = 0 and dV = dO
+    q, k, v, do, cu = _bwd_case(3, lengths=(1, 1, 1), H=2, d=5)
+    dq, dk, dv = oracle.varlen_bwd(q, k, v, do, cu, 0.9)
+    assert np.all(dq == 0.0) and np.all(dk == 0.0)
+    np.testing.assert_array_equal(dv, do)
+    # values constant over a segment: O does not depend on the weights, so dQ = dK = 0,
+    # and dV_j = sum_i P_ij dO_i sums (over keys) to the segment's total dO
+    q, k, v, do, cu = _bwd_case(4, lengths=(6, 4), H=1, d=3)
+    v[:6] = 1.5
+    v[6:] = -2.0
+    dq, dk, dv = oracle.varlen_bwd(q, k, v, do, cu, 1.1)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dv[:6].sum(axis=0), do[:6].sum(axis=0), atol=1e-13)
+    np.testing.assert_allclose(dv[6:].sum(axis=0), do[6:].sum(axis=0), atol=1e-13)
+
+
+def test_backward_key_gradients_sum_to_zero_per_segment():
+    # every row of dS sums to zero (softmax Jacobian), so sum_j dK_j = scale sum_i q_i
+    # sum_j dS_ij = 0 within each segment and head
+    q, k, v, do, cu = _bwd_case(5, lengths=(40, 3, 17), H=2, d=8)
+    _, dk, _ = oracle.varlen_bwd(q, k, v, do, cu, 0.6)
+    for s in range(3):
+        tot = dk[cu[s]:cu[s + 1]].sum(axis=0)
+        np.testing.assert_allclose(tot, 0.0, atol=1e-12)
+
+
+def test_backward_pack_equals_each_segment_alone():
+    q, k, v, do, cu = _bwd_case(6, lengths=(7, 0, 12, 3), H=2, d=4)
+    full = oracle.varlen_bwd(q, k, v, do, cu, 0.5)
+    for s in range(4):
+        sl = slice(int(cu[s]), int(cu[s + 1]))
+        if sl.stop == sl.start:
+            continue
+        one = oracle.varlen_bwd(q[sl], k[sl], v[sl], do[sl],
+                                np.array([0, sl.stop - sl.start], np.int32), 0.5)
+        for a, b in zip(full, one):
+            np.testing.assert_array_equal(a[sl], b)
