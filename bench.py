@@ -14,6 +14,7 @@ row sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C3] [--no-cpu-baseline]
     python bench.py --config X1          # separate q/k tables: long-Q, short-KV cross-attention
     python bench.py --op merge           # (O, LSE) merge of two results, C3's shape
+    python bench.py --op bwd             # backward (dQ, dK, dV) on the same pack
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -241,13 +242,75 @@ def bench_merge(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_bwd(args):
+    """Backward of the forward on the same pack: three kernels per step (row statistics,
+    dK/dV, dQ).  Counted work 10*sum(L^2)*H*d (five L x L x d matmuls, the usual count);
+    this design executes seven (S and dP are recomputed in each of the two passes)."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import pfa_varlen_bwd, pfa_varlen_fwd
+    wl = W.generate(args.config, seed=args.seed)
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    rng = np.random.default_rng(1000 + args.seed)
+    do_bits = W.bf16_bits(rng.standard_normal(wl.q.shape, dtype=np.float32))
+    do = up(do_bits)
+    stream = torch.cuda.current_stream(dev)
+    out, lse = pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty((2, wl.heads, wl.total_tokens), dtype=torch.float32, device=dev)
+
+    def step():
+        pfa_varlen_bwd(q, k, v, out, do, lse, cu, wl.max_seqlen, wl.scale, dq=dq, dk=dk, dv=dv,
+                       workspace=ws, stream=stream)
+
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    counted = 2.5 * wl.flops
+    executed = 3.5 * wl.flops
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        heads = [0, wl.heads - 1]
+        sl = lambda a: np.ascontiguousarray(a[:, heads])
+        t0 = time.perf_counter()
+        refs = oracle.varlen_bwd(sl(wl.q), sl(wl.k), sl(wl.v), sl(do_bits), wl.cu_seqlens, wl.scale)
+        dt = time.perf_counter() - t0
+        flop = counted * len(heads) / wl.heads
+        parity = {}
+        for name, t, r in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+            g = W.bf16_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16)[:, heads])
+            d = g - r
+            parity[name] = {"rel_rms": float(np.sqrt((d * d).sum() / (r * r).sum())),
+                            "max_err_over_max_ref": float(np.abs(d).max() / np.abs(r).max())}
+        cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"heads {heads} of {wl.name} (every segment), "
+                                           f"{flop / 1e9:.1f} GFLOP counted in {dt:.1f} s"}
+    achieved = counted / (kms * 1e-3) / 1e12
+    rec = {"metric": "attention backward TFLOP/s (10·ΣL_i²·H·d counted) and % of bf16 MFMA peak, 1 GPU",
+           "value": round(counted / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V and dO; no dataset or weights)",
+           "config": {"workload": describe(wl), "segments": list(wl.lengths),
+                      "total_tokens": wl.total_tokens, "heads": wl.heads, "head_dim": wl.head_dim,
+                      "counted_flop_per_step": counted, "executed_mfma_flop_per_step": executed,
+                      "seed": args.seed},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "executed_frac": round(achieved * 1.4 / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5)},
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
-    ap.add_argument("--op", default="fwd", choices=["fwd", "merge"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -266,6 +329,9 @@ def main():
         return
     if args.op == "merge":
         bench_merge(args)
+        return
+    if args.op == "bwd":
+        bench_bwd(args)
         return
     if args.config in W.CROSS_CONFIGS:
         bench_cross(args)

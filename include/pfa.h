@@ -136,6 +136,32 @@ PFA_API int pfa_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
                            void* out, float* lse, hipStream_t stream);
 
 /*
+ * pfa_varlen_bwd -- gradients of pfa_varlen_fwd (self-attention, one segment table).
+ *
+ * The pages train with this packed path (Mage-Flow page: the gains of packing are
+ * training throughput) but print no gradient formulas; the operation is the chain rule of
+ * the forward definition above.  For upstream gradient dO of O, per segment and head,
+ * with P the softmax rows (recomputed from lse) and s_ij = scale q_i.k_j:
+ *     dV = P^T dO,   dP = dO V^T,   delta_i = dO_i . O_i (= sum_j P_ij dP_ij),
+ *     dS = P * (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
+ *
+ * q, k, v, out, dout  device bf16 [T, heads, head_dim] (out: the forward's output).
+ * lse         device fp32 [heads, T]: the forward's LSE (natural log).  Required.
+ * cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale: as for pfa_varlen_fwd.
+ * dq, dk, dv  device bf16 [T, heads, head_dim], written (round to nearest even).
+ * workspace   device fp32 [2, heads, T], written: -lse*log2(e) and delta.  The caller
+ *             owns it; its contents after the call are not part of the interface.
+ * Ownership and errors as for pfa_varlen_fwd; PFA_ERR_ALIAS if an output (dq, dk, dv,
+ * workspace) is an input or another output.  Three kernels are enqueued on stream (a
+ * row-statistics pass, the dK/dV pass, the dQ pass); no atomics, so results are
+ * deterministic.
+ */
+PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, const int32_t* cu_seqlens,
+                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
+                           void* dq, void* dk, void* dv, float* workspace, hipStream_t stream);
+
+/*
  * pfa_check_cu_seqlens -- host-side validator of a cu_seqlens table (no device calls).
  *
  * cu_host     host pointer to num_seqs + 1 int32 values.

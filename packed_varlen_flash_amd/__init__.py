@@ -14,7 +14,8 @@ import numpy as np
 
 from . import _lib
 
-__all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_attn_merge", "pfa_check_cu_seqlens",
+__all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_bwd", "pfa_attn_merge",
+           "pfa_check_cu_seqlens",
            "pfa_status_string", "PfaError", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -163,3 +164,43 @@ def pfa_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, want_lse: bool = 
     if rc != 0:
         raise PfaError(rc)
     return out, lse
+
+
+def pfa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int,
+                   scale: float | None = None, dq=None, dk=None, dv=None, workspace=None,
+                   stream=None):
+    """Gradients (dq, dk, dv) of pfa_varlen_fwd for upstream gradient ``dout``.
+    q, k, v, out, dout: bf16 [T, H, d]; lse: the forward's fp32 [H, T]; cu_seqlens int32.
+    ``workspace`` (fp32 [2, H, T]) is allocated when not given."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_bf16(name, t, torch)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    _check_table("cu_seqlens", cu_seqlens, torch)
+    T, H, d = q.shape
+    if lse is None or lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous fp32 [H, T]")
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bf16(name, t, torch)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    if workspace is None:
+        workspace = torch.empty((2, H, T), dtype=torch.float32, device=q.device)
+    elif workspace.numel() < 2 * H * T or workspace.dtype != torch.float32 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous fp32 tensor of >= 2*H*T elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, int(max_seqlen), H, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return dq, dk, dv

@@ -20,6 +20,8 @@ _SIGNATURES = {
     "pfa_attn_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "pfa_varlen_bwd": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 +
+                       [ctypes.c_float] + [ctypes.c_void_p] * 5),
     "pfa_check_cu_seqlens": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_void_p]),
     "pfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

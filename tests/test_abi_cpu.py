@@ -26,8 +26,9 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_attn_merge",
-                                       "pfa_check_cu_seqlens", "pfa_status_string"}
+    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_bwd",
+                                       "pfa_attn_merge", "pfa_check_cu_seqlens",
+                                       "pfa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -103,6 +104,27 @@ def test_merge_argument_checks_run_before_any_hip_call(lib):
     assert _merge(lib, out=9, lse=9) == -7     # out and lse the same buffer
     assert _merge(lib, total=0) == 0           # nothing to do, nothing launched
     assert _merge(lib, total=2**31, heads=1) == -11
+
+
+def _bwd(lib, q=1, k=2, v=3, out=4, dout=5, lse=6, cu=7, num_seqs=1, max_seqlen=1, heads=1,
+         head_dim=128, scale=1.0, dq=8, dk=9, dv=10, ws=11):
+    return lib.pfa_varlen_bwd(q, k, v, out, dout, lse, cu, num_seqs, max_seqlen, heads, head_dim,
+                              scale, dq, dk, dv, ws, None)
+
+
+def test_bwd_argument_checks_run_before_any_hip_call(lib):
+    for name in ("q", "k", "v", "out", "dout", "lse", "cu", "dq", "dk", "dv", "ws"):
+        assert _bwd(lib, **{name: None}) == -1, name
+    assert _bwd(lib, num_seqs=0) == -2
+    assert _bwd(lib, heads=0) == -3
+    assert _bwd(lib, max_seqlen=0) == -4
+    assert _bwd(lib, head_dim=32) == -5
+    assert _bwd(lib, scale=0.0) == -6
+    assert _bwd(lib, dq=1) == -7          # output is an input
+    assert _bwd(lib, ws=6) == -7          # workspace is the LSE
+    assert _bwd(lib, dk=8) == -7          # two outputs share a buffer
+    assert _bwd(lib, ws=10) == -7
+    assert _bwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
 
 
 def test_host_validator(lib):

@@ -1,0 +1,117 @@
+"""GPU parity of the backward (pfa_varlen_bwd) against the fp64 oracle's gradients.
+
+No bar for gradients is given with the forward's; these bounds are derived from the
+arithmetic.  Each gradient element is rounded once to bf16 (half a spacing, at most
+2^-8 relative; about 1.6e-3 relative RMS on its own), and the kernel feeds bf16-rounded
+P and dS (each at most 2^-8 relative per element, averaging out over a row) to the MFMAs
+and uses the forward's bf16 output in delta.  So the relative RMS of each tensor gets the
+forward's 4e-3 bar, and the worst element is bounded relative to the tensor's largest
+gradient by the forward's 1e-2.  Measured on these cases: relative RMS 2.0e-3 to 3.3e-3
+(sharp heads highest), worst element at most 5.4e-3 of max|g|."""
+import numpy as np
+import pytest
+
+import oracle
+import pfa_workloads as W
+from tests._gpu import from_dev_bf16, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_RMS = 4e-3      # per tensor: ||g - g_ref|| / ||g_ref||
+GRAD_MAX_REL = 1e-2      # per tensor: max|g - g_ref| / max|g_ref|
+
+
+def _dout(wl, seed):
+    rng = np.random.default_rng(1000 + seed)
+    return W.bf16_bits(rng.standard_normal((wl.total_tokens, wl.heads, wl.head_dim), dtype=np.float32))
+
+
+def _run(wl, dout_bits, label):
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_bwd, pfa_varlen_fwd
+    say(f"[gpu] pfa_varlen_bwd {label}: segs={len(wl.lengths)} T={wl.total_tokens} H={wl.heads} "
+        f"d={wl.head_dim} max_seqlen={wl.max_seqlen}")
+    q, k, v = to_dev(wl.q), to_dev(wl.k), to_dev(wl.v)
+    cu = torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to("cuda")
+    out, lse = pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale)
+    do = to_dev(dout_bits)
+    dq, dk, dv = pfa_varlen_bwd(q, k, v, out, do, lse, cu, wl.max_seqlen, wl.scale)
+    torch.cuda.synchronize()
+    return [from_dev_bf16(t) for t in (dq, dk, dv)]
+
+
+def _metrics(bits, ref):
+    g = W.bf16_to_f64(bits)
+    d = g - ref
+    nref = float(np.sqrt((ref * ref).sum()))
+    mref = float(np.abs(ref).max())
+    return (float(np.sqrt((d * d).sum())) / nref if nref > 0 else float(np.sqrt((d * d).sum())),
+            float(np.abs(d).max()) / mref if mref > 0 else float(np.abs(d).max()))
+
+
+def _check(wl, dout_bits, label, heads=None):
+    got = _run(wl, dout_bits, label)
+    if heads is None:
+        refs = oracle.varlen_bwd(wl.q, wl.k, wl.v, dout_bits, wl.cu_seqlens, wl.scale)
+    else:
+        sl = lambda a: np.ascontiguousarray(a[:, heads])
+        refs = oracle.varlen_bwd(sl(wl.q), sl(wl.k), sl(wl.v), sl(dout_bits), wl.cu_seqlens, wl.scale)
+        got = [g[:, heads] for g in got]
+    worst = []
+    for name, g, r in zip(("dq", "dk", "dv"), got, refs):
+        rr, mr = _metrics(g, r)
+        worst.append((name, rr, mr))
+    say("[grad] " + label + ": " + "  ".join(f"{n} relRMS={a:.3e} maxrel={b:.3e}" for n, a, b in worst))
+    for n, a, b in worst:
+        assert a <= GRAD_REL_RMS, (n, a)
+        assert b <= GRAD_MAX_REL, (n, b)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_ragged_packs(seed):
+    rng = np.random.default_rng(300 + seed)
+    d = 64 if seed % 2 else 128
+    lengths = W.random_lengths(rng, int(rng.integers(1, 6)), 700)
+    if sum(lengths) == 0:
+        lengths[0] = 5
+    wl = W.make(lengths, 3, d, seed=300 + seed)
+    _check(wl, _dout(wl, seed), f"ragged seed={seed} d={d} lengths={lengths}")
+
+
+@pytest.mark.parametrize("lengths", [[1, 2, 3], [64], [65], [127, 128, 129], [255, 256, 257]])
+def test_tile_boundaries(lengths):
+    wl = W.make(lengths, 2, 128, seed=7)
+    _check(wl, _dout(wl, 7), f"boundaries {lengths}")
+
+
+def test_c3_shape_on_two_heads():
+    wl = W.generate("C3")
+    _check(wl, _dout(wl, 3), "C3 heads 0 and 23", heads=[0, 23])
+
+
+def test_sharp_heads():
+    wl = W.make([1024, 700], 24, 128, seed=9, per_head_qk_scale=True)
+    _check(wl, _dout(wl, 9), "sharp heads 0, 12, 23", heads=[0, 12, 23])
+
+
+def test_run_to_run_bitwise_determinism():
+    wl = W.make([513, 1, 300, 1024], 2, 128, seed=11)
+    do = _dout(wl, 11)
+    a = _run(wl, do, "determinism #1")
+    b = _run(wl, do, "determinism #2")
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_pack_equals_each_segment_alone_bitwise():
+    wl = W.make([300, 129, 1, 700], 2, 64, seed=12)
+    do = _dout(wl, 12)
+    full = _run(wl, do, "pack")
+    for s, L in enumerate(wl.lengths):
+        a, b = int(wl.cu_seqlens[s]), int(wl.cu_seqlens[s + 1])
+        one = W.Workload(name="alone", q=wl.q[a:b], k=wl.k[a:b], v=wl.v[a:b],
+                         cu_seqlens=np.array([0, L], np.int32), lengths=(L,), heads=wl.heads,
+                         head_dim=wl.head_dim, scale=wl.scale, max_seqlen=L, seed=0)
+        alone = _run(one, np.ascontiguousarray(do[a:b]), f"segment {s} alone")
+        for x, y in zip(full, alone):
+            assert np.array_equal(x[a:b], y)
