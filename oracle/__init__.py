@@ -17,6 +17,13 @@ marshals:
   disjoint key sets from the results over each (fp64, see its docstring).
 * ``varlen_bwd(q, k, v, dout, cu_seqlens, scale)`` -> ``(dq, dk, dv)`` fp64 ``[T, H, d]``:
   the gradients of the self-attention forward for upstream gradient ``dout``.
+* ``rope(x, cos, sin)``: rotary position embedding of ``x`` [T, H, d] with per-token
+  angle tables ``cos``, ``sin`` [T, d/2] (rotate-half pairs), fp64.
+* ``qkv_rope_fwd(qkv, cu_seqlens, scale, cos=None, sin=None, rows=None)``: attention on a
+  fused ``[T, 3, H, d]`` bf16 projection output, with q and k rotated and rounded to bf16
+  first when tables are given.
+* ``widen_bf16(bits)`` / ``round_bf16_bits(x)``: bf16 bits to fp64 and back (one
+  rounding, ties to even).
 * ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
   probability matrix over all ``T`` tokens (zero off-segment).
 
@@ -169,6 +176,58 @@ def varlen_bwd(q, k, v, dout, cu_seqlens, scale: float):
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (code {rc})")
     return dq, dk, dv
+
+
+def rope(x, cos, sin):
+    """Rotary position embedding, rotate-half pairing: for i < d/2,
+        y[i]       = x[i] cos_i - x[i + d/2] sin_i
+        y[i + d/2] = x[i + d/2] cos_i + x[i] sin_i,
+    with the token's own angle table row (the same rotation for every head).  The pages
+    place RoPE between the QKV projection and attention in the DiT block (Mage-Flow page,
+    section on fusion opportunities in the DiT block) without fixing the variant; the
+    rotate-half pairing and caller-supplied per-token tables (1-D, 2-D axial or any other
+    position scheme reduces to them) are the reading taken.  fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    c = np.asarray(cos, dtype=np.float64)[:, None, :]
+    s = np.asarray(sin, dtype=np.float64)[:, None, :]
+    half = x.shape[2] // 2
+    a, b = x[:, :, :half], x[:, :, half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=2)
+
+
+def qkv_rope_fwd(qkv_bits, cu_seqlens, scale: float, cos=None, sin=None, rows=None):
+    """Attention on the fused projection output qkv [T, 3, H, d] (bf16 bits): q, k and v
+    are its three consecutive chunks along the feature axis (the merged W_qkv projection
+    of the Mage-Flow page, section on fusion opportunities in the DiT block, split into
+    three with chunk(3, dim=-1)).  With angle tables, q and k are rotated (``rope``) and
+    rounded to bf16, as a pipeline that stores them between the two steps would, before
+    the attention of ``varlen_fwd``."""
+    qkv = np.asarray(qkv_bits)
+    if qkv.dtype != np.uint16 or qkv.ndim != 4 or qkv.shape[1] != 3:
+        raise ValueError("expected qkv as bf16 bits [T, 3, H, d]")
+    q, k, v = (np.ascontiguousarray(qkv[:, i]) for i in range(3))
+    if (cos is None) != (sin is None):
+        raise ValueError("give both angle tables or neither")
+    if cos is not None:
+        q = round_bf16_bits(rope(widen_bf16(q), cos, sin))
+        k = round_bf16_bits(rope(widen_bf16(k), cos, sin))
+    return varlen_fwd(q, k, v, cu_seqlens, scale, rows=rows)
+
+
+def widen_bf16(bits):
+    """bf16 bit patterns -> their exact fp64 values."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def round_bf16_bits(x):
+    """fp64 -> bf16 bit patterns, one rounding to nearest, ties to even, for values in
+    bf16's normal range (and zero): bf16 keeps 8 significant bits, so x = m 2^e with
+    0.5 <= |m| < 1 becomes rint(m 2^8) 2^(e-8); the result is exact in fp32, whose upper
+    half is the bf16 pattern."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    r = np.ldexp(np.rint(m * 256.0), e - 8).astype(np.float32)
+    return (r.view(np.uint32) >> 16).astype(np.uint16)
 
 
 def merge(o_a, lse_a, o_b, lse_b):

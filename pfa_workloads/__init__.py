@@ -223,6 +223,44 @@ def generate_cross(name: str, seed: int = 0) -> CrossWorkload:
                       name=name)
 
 
+# ------------------------------------------------- fused QKV input and angle tables
+
+def grid_positions(lengths) -> tuple:
+    """(row, col) patch coordinates of every packed token: a segment of L tokens is an
+    image laid out row-major on a grid ceil(sqrt(L)) patches wide (4096 -> 64 x 64,
+    1296 -> 36 x 36), restarting at (0, 0) for every segment."""
+    rows, cols = [], []
+    for L in lengths:
+        L = int(L)
+        w = max(1, math.isqrt(L - 1) + 1) if L > 0 else 1
+        i = np.arange(L, dtype=np.int64)
+        rows.append(i // w)
+        cols.append(i % w)
+    if not rows:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(rows), np.concatenate(cols)
+
+
+def rope_tables_2d(lengths, head_dim: int, base: float = 10000.0) -> tuple:
+    """Axial 2-D rotary angle tables (cos, sin), float32 [T, head_dim / 2]: the first half
+    of the head_dim / 2 frequency pairs turns with the patch row, the second half with
+    the patch column, at frequencies base^(-j / (head_dim / 4)), j = 0 .. head_dim/4 - 1.
+    Angles are formed in fp64 and their cosine and sine rounded once to float32."""
+    if head_dim % 4:
+        raise ValueError("head_dim must be a multiple of 4")
+    r, c = grid_positions(lengths)
+    nf = head_dim // 4
+    freq = base ** (-np.arange(nf, dtype=np.float64) / nf)
+    ang = np.concatenate([r[:, None] * freq[None, :], c[:, None] * freq[None, :]], axis=1)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def fuse_qkv(q, k, v) -> np.ndarray:
+    """[T, 3, H, d] bf16 bits: the layout of one projection whose output features are q,
+    then k, then v (row t holds 3 * H * d consecutive values)."""
+    return np.ascontiguousarray(np.stack([q, k, v], axis=1))
+
+
 def sample_rows(cu_seqlens, stride: int = 61, edge: int = 128, full_upto: int = 4096) -> np.ndarray:
     """Deterministic row sample for configurations too large for the oracle in full.
 

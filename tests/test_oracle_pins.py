@@ -530,3 +530,121 @@ def test_backward_pack_equals_each_segment_alone():
                                 np.array([0, sl.stop - sl.start], np.int32), 0.5)
         for a, b in zip(full, one):
             np.testing.assert_array_equal(a[sl], b)
+
+
+# ------------------------------------------------- fused QKV input with rotary prologue
+# Mage-Flow page, section on fusion opportunities in the DiT block: one W_qkv projection
+# whose output is split into q, k, v by chunk(3, dim=-1), then RoPE, then attention.
+# The rotary variant is the rotate-half pairing (i, i + d/2) with per-token angle tables.
+
+def test_bf16_rounding_is_one_rounding_to_nearest_even():
+    cases = {
+        1.0 + 2.0 ** -8: 0x3F80,                     # tie, even neighbour below
+        1.0 + 3 * 2.0 ** -8: 0x3F82,                 # tie, even neighbour above
+        -(1.0 + 2.0 ** -8): 0xBF80,
+        1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81,        # just above the tie
+        1.0 + 2.0 ** -8 + 2.0 ** -25: 0x3F81,        # fp32 first would make this a tie -> 0x3F80
+        0.0: 0x0000,
+        3.0: 0x4040,
+        255.5: 0x4380,                               # 8 significant bits: 255.5 -> 256
+    }
+    got = oracle.round_bf16_bits(np.array(list(cases.keys())))
+    assert [int(g) for g in got] == list(cases.values())
+    # on fp32 inputs (one rounding either way) it agrees with the generator's own rounding
+    x = np.random.default_rng(5).standard_normal(20000).astype(np.float32) * 37.0
+    np.testing.assert_array_equal(oracle.round_bf16_bits(x.astype(np.float64)), W.bf16_bits(x))
+    np.testing.assert_array_equal(oracle.widen_bf16(W.bf16_bits(x)),
+                                  W.bf16_to_f64(W.bf16_bits(x)))
+
+
+def test_rope_is_complex_rotation_of_half_pairs():
+    rng = np.random.default_rng(11)
+    T, H, d = 9, 3, 16
+    x = rng.standard_normal((T, H, d))
+    ang = rng.uniform(-10, 10, size=(T, d // 2))
+    y = oracle.rope(x, np.cos(ang), np.sin(ang))
+    z = torch.complex(torch.from_numpy(x[..., : d // 2]), torch.from_numpy(x[..., d // 2:]))
+    zr = z * torch.polar(torch.ones(T, 1, d // 2, dtype=torch.float64),
+                         torch.from_numpy(ang)[:, None, :])
+    np.testing.assert_allclose(y[..., : d // 2], zr.real.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[..., d // 2:], zr.imag.numpy(), rtol=0, atol=1e-13)
+
+
+def test_rope_special_angles_compose_and_keep_pair_norms():
+    rng = np.random.default_rng(12)
+    T, H, d = 5, 2, 8
+    x = rng.standard_normal((T, H, d))
+    one, zero = np.ones((T, d // 2)), np.zeros((T, d // 2))
+    np.testing.assert_array_equal(oracle.rope(x, one, zero), x)          # angle 0
+    quarter = oracle.rope(x, zero, one)                                  # angle pi/2
+    np.testing.assert_array_equal(quarter[..., :4], -x[..., 4:])
+    np.testing.assert_array_equal(quarter[..., 4:], x[..., :4])
+    a, b = rng.uniform(-3, 3, (T, d // 2)), rng.uniform(-3, 3, (T, d // 2))
+    two = oracle.rope(oracle.rope(x, np.cos(a), np.sin(a)), np.cos(b), np.sin(b))
+    np.testing.assert_allclose(two, oracle.rope(x, np.cos(a + b), np.sin(a + b)), atol=1e-13)
+    y = oracle.rope(x, np.cos(a), np.sin(a))
+    np.testing.assert_allclose(y[..., :4] ** 2 + y[..., 4:] ** 2, x[..., :4] ** 2 + x[..., 4:] ** 2,
+                               atol=1e-13)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    # 1-D positions p with angles p * w_j: q at m and k at n score like q at m+s, k at n+s
+    rng = np.random.default_rng(13)
+    d = 32
+    w = 10000.0 ** (-np.arange(d // 2) / (d // 2))
+    q, k = rng.standard_normal((1, 1, d)), rng.standard_normal((1, 1, d))
+
+    def score(m, n):
+        am, an = (m * w)[None], (n * w)[None]
+        return float(np.sum(oracle.rope(q, np.cos(am), np.sin(am)) *
+                            oracle.rope(k, np.cos(an), np.sin(an))))
+    for m, n, s in [(0, 3, 7), (5, 1, 100), (12, 12, 33)]:
+        assert abs(score(m, n) - score(m + s, n + s)) < 1e-10
+    assert abs(score(0, 3) - score(0, 4)) > 1e-3
+
+
+def test_fused_qkv_chunks_are_q_then_k_then_v():
+    w = W.make([13, 0, 40, 7], heads=3, head_dim=64, seed=21)
+    qkv = W.fuse_qkv(w.q, w.k, w.v)
+    assert qkv.shape == (w.total_tokens, 3, 3, 64)
+    o, l = oracle.qkv_rope_fwd(qkv, w.cu_seqlens, w.scale)
+    o_ref, l_ref = oracle.varlen_fwd(w.q, w.k, w.v, w.cu_seqlens, w.scale)
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(l, l_ref)
+    o_swap, _ = oracle.varlen_fwd(w.q, w.v, w.k, w.cu_seqlens, w.scale)
+    assert np.max(np.abs(o - o_swap)) > 0.1
+
+
+def test_fused_qkv_rope_with_exact_quarter_turns():
+    # angles of whole quarter turns rotate bf16 values exactly, so the expected attention
+    # is the plain attention of q and k rotated by complex multiplication with i^n
+    w = W.make([33, 1, 70], heads=2, head_dim=64, seed=22)
+    T, d = w.total_tokens, 64
+    turns = np.random.default_rng(23).integers(0, 4, size=(T, d // 2))
+    cos = np.cos(turns * np.pi / 2).round()
+    sin = np.sin(turns * np.pi / 2).round()
+    o, l = oracle.qkv_rope_fwd(W.fuse_qkv(w.q, w.k, w.v), w.cu_seqlens, w.scale, cos, sin)
+
+    def turn(bits):
+        x = torch.from_numpy(W.bf16_to_f64(bits))
+        z = torch.complex(x[..., : d // 2], x[..., d // 2:]) * \
+            (torch.tensor(1j, dtype=torch.complex128) ** torch.from_numpy(turns)[:, None, :])
+        return W.bf16_bits(torch.cat([z.real, z.imag], -1).numpy().astype(np.float32))
+    o_ref, l_ref = oracle.varlen_fwd(turn(w.q), turn(w.k), w.v, w.cu_seqlens, w.scale)
+    np.testing.assert_array_equal(o, o_ref)
+    np.testing.assert_array_equal(l, l_ref)
+    o_plain, _ = oracle.varlen_fwd(w.q, w.k, w.v, w.cu_seqlens, w.scale)
+    assert np.max(np.abs(o - o_plain)) > 0.1
+
+
+def test_fused_qkv_rope_rounds_rotated_q_and_k_to_bf16():
+    w = W.make([20, 9], heads=2, head_dim=64, seed=24)
+    cos, sin = W.rope_tables_2d(w.lengths, 64)
+    o, _ = oracle.qkv_rope_fwd(W.fuse_qkv(w.q, w.k, w.v), w.cu_seqlens, w.scale, cos, sin)
+    qr = oracle.rope(W.bf16_to_f64(w.q), cos, sin)
+    kr = oracle.rope(W.bf16_to_f64(w.k), cos, sin)
+    o_exact, _ = oracle.varlen_fwd(qr, kr, W.bf16_to_f64(w.v), w.cu_seqlens, w.scale)
+    diff = np.max(np.abs(o - o_exact))
+    assert 0 < diff < 2e-2      # only the bf16 rounding of the rotated q and k separates them
+    with pytest.raises(ValueError):
+        oracle.qkv_rope_fwd(W.fuse_qkv(w.q, w.k, w.v), w.cu_seqlens, w.scale, cos, None)

@@ -48,3 +48,14 @@ def test_row_sample():
     assert rows[0] == 0 and 4999 in rows and 63 in rows and 64 not in rows and 61 in rows
     assert np.all(np.isin(np.arange(5000, 5100), rows))
     assert np.all(np.diff(rows) > 0)
+
+
+def test_grid_positions_and_rope_tables():
+    r, c = W.grid_positions([4096, 1296, 5])
+    assert (r[4095], c[4095]) == (63, 63) and (r[4096 + 1295], c[4096 + 1295]) == (35, 35)
+    assert list(r[-5:]) == [0, 0, 0, 1, 1] and list(c[-5:]) == [0, 1, 2, 0, 1]
+    cos, sin = W.rope_tables_2d([4096, 5], 128)
+    assert cos.shape == (4101, 64) and cos.dtype == np.float32
+    assert np.all(cos[0] == 1) and np.all(sin[0] == 0) and np.all(cos[4096] == 1)
+    np.testing.assert_allclose(cos ** 2 + sin ** 2, 1, atol=1e-6)
+    assert sin[70, 0] == np.float32(np.sin(1.0)) and sin[70, 32] == np.float32(np.sin(6.0))
