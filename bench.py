@@ -15,6 +15,7 @@ row sample of the same workload.
     python bench.py --config X1          # separate q/k tables: long-Q, short-KV cross-attention
     python bench.py --op merge           # (O, LSE) merge of two results, C3's shape
     python bench.py --op bwd             # backward (dQ, dK, dV) on the same pack
+    python bench.py --op qkv             # fused [T,3,H,d] input with 2-D RoPE, same pack
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -304,13 +305,102 @@ def bench_bwd(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_qkv(args):
+    """The forward read straight from a fused [T, 3, H, d] projection output, with 2-D axial
+    RoPE on q and k: one step is the key rotation pass plus the attention kernel.  Beside
+    it, the same work without the fusion (separate contiguous q, k, v copies and RoPE in
+    PyTorch ops, then the plain forward) is timed for comparison."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import pfa_varlen_fwd, pfa_varlen_fwd_qkv
+    wl = W.generate(args.config, seed=args.seed)
+    T, H, d = wl.total_tokens, wl.heads, wl.head_dim
+    cos_np, sin_np = W.rope_tables_2d(wl.lengths, d)
+    qkv_np = W.fuse_qkv(wl.q, wl.k, wl.v)
+    dev = torch.device("cuda:0")
+    qkv = torch.from_numpy(qkv_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    cos, sin = torch.from_numpy(cos_np).to(dev), torch.from_numpy(sin_np).to(dev)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    k_rot = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pfa_varlen_fwd_qkv(qkv, cu, wl.max_seqlen, wl.scale, cos, sin, out=out, lse=lse, k_rot=k_rot,
+                           stream=stream)
+
+    def step_plain():      # fused input, no rotation: the attention kernel alone
+        pfa_varlen_fwd_qkv(qkv, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
+
+    c32, s32 = cos[:, None, :], sin[:, None, :]
+
+    def rope_torch(x):
+        x = x.float()
+        a, b = x[..., : d // 2], x[..., d // 2:]
+        return torch.cat([a * c32 - b * s32, b * c32 + a * s32], -1).to(torch.bfloat16)
+
+    def step_unfused():
+        q3, k3, v3 = qkv.unbind(1)
+        pfa_varlen_fwd(rope_torch(q3), rope_torch(k3), v3.contiguous(), cu, wl.max_seqlen, wl.scale,
+                       out=out, lse=lse, stream=stream)
+
+    ms_plain, kms_plain = timed(step_plain, stream, args.steps, args.warmup)
+    ms_unf, _ = timed(step_unfused, stream, args.steps, args.warmup)
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    rot_bytes = T * (4 * H * d + 4 * d)          # read k, both tables; write rotated k
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(1234)
+        pilot = np.sort(rng.choice(T, size=24, replace=False))
+        t0 = time.perf_counter()
+        oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale, rows=pilot)
+        per_row = (time.perf_counter() - t0) / len(pilot)
+        n = int(max(24, min(T, args.cpu_budget / max(per_row, 1e-9))))
+        rows = np.sort(rng.choice(T, size=n, replace=False))
+        t0 = time.perf_counter()
+        o_ref, l_ref = oracle.qkv_rope_fwd(qkv_np, wl.cu_seqlens, wl.scale, cos_np, sin_np, rows=rows)
+        dt = time.perf_counter() - t0
+        seg = np.searchsorted(wl.cu_seqlens[1:], rows, side="right")
+        flop = 4.0 * float(np.diff(wl.cu_seqlens)[seg].astype(np.float64).sum()) * H * d
+        o = W.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        dd = np.abs(o - o_ref)
+        parity = {"rows": int(n), "max_abs_err": float(dd.max()),
+                  "rel_rms": float(np.sqrt((dd * dd).sum() / (o_ref * o_ref).sum())),
+                  "lse_max_abs_err": float(np.abs(lse.cpu().numpy()[:, rows] - l_ref).max())}
+        cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{n} uniformly drawn query rows of {wl.name} (all heads), after the "
+                         f"fp64 rotation of every q and k: {flop / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    achieved = wl.flops / (kms * 1e-3) / 1e12
+    rec = {"metric": "fused-QKV + RoPE attention TFLOP/s (4·ΣL_i²·H·d), 1 GPU",
+           "value": round(wl.flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) bf16 q/k/v in one [T,3,H,d] tensor; 2-D axial "
+                   "rotary tables from each image's patch grid)",
+           "config": {"workload": f"{describe(wl)}; fused [T,3,H,d] input, 2-D RoPE",
+                      "segments": list(wl.lengths), "total_tokens": T, "heads": H, "head_dim": d,
+                      "flop_per_step": wl.flops, "rotation_pass_bytes": rot_bytes,
+                      "seed": args.seed},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5),
+                        "kernel_ms_covers": "key rotation pass + attention kernel"},
+           "without_rotation_ms": round(ms_plain, 5),
+           "unfused_torch_ms": round(ms_unf, 5),
+           "speedup_vs_unfused": round(ms_unf / ms, 3),
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
-    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -329,6 +419,9 @@ def main():
         return
     if args.op == "merge":
         bench_merge(args)
+        return
+    if args.op == "qkv":
+        bench_qkv(args)
         return
     if args.op == "bwd":
         bench_bwd(args)

@@ -43,7 +43,9 @@ typedef enum pfa_status {
   PFA_ERR_CU_SEQLENS = -8,    /* host validator: malformed cu_seqlens table              */
   PFA_ERR_DEVICE = -9,        /* no usable device, or a device query failed              */
   PFA_ERR_LAUNCH = -10,       /* the kernel launch reported an error                     */
-  PFA_ERR_SIZE = -11          /* heads * head_dim or the table exceeds the int32 range   */
+  PFA_ERR_SIZE = -11,         /* a row (heads * head_dim, 3x that for a fused input) over
+                                 2^23 elements, or more than 2^31 - 1 work slots or rows */
+  PFA_ERR_ALIGN = -12         /* a buffer that must be 16-byte aligned is not            */
 } pfa_status;
 
 /*
@@ -111,6 +113,42 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v,
                               int num_seqs, int max_seqlen_q, int max_seqlen_k, int heads,
                               int head_dim, float scale, void* out, float* lse,
                               hipStream_t stream);
+
+/*
+ * pfa_varlen_fwd_qkv -- the self-attention forward read straight from a fused projection
+ * output, with optional rotary position embedding of q and k.
+ *
+ * The DiT block of the Mage-Flow page (section on its fusion opportunities) computes q, k
+ * and v with one merged W_qkv projection, splits its output into three along the feature
+ * axis (chunk(3, dim=-1)), applies RoPE, then attention.  This call takes that output as
+ * it is: q, k and v are read through a row stride of 3 * heads * head_dim, with no copy
+ * into separate tensors.  The pages do not fix the RoPE variant; this is the rotate-half
+ * pairing: for i < head_dim / 2, features (x_i, x_{i + head_dim/2}) of token t, every
+ * head, become
+ *     (x_i cos[t][i] - x_{i+d/2} sin[t][i],  x_{i+d/2} cos[t][i] + x_i sin[t][i]),
+ * evaluated in fp32 and rounded to bf16 (nearest even) before the attention of
+ * pfa_varlen_fwd.  Per-token tables cover any position scheme (1-D, axial 2-D or 3-D):
+ * the caller writes each token's angles.
+ *
+ * qkv         device bf16 [T, 3, heads, head_dim] (row t: q, then k, then v, each
+ *             heads * head_dim values, head-major); 16-byte aligned.  Read only.
+ * rope_cos, rope_sin   device fp32 [T, head_dim / 2], 16-byte aligned, or both NULL for
+ *             no rotation.
+ * k_rot       with tables: device bf16 [T, heads, head_dim] workspace, 16-byte aligned,
+ *             owned by the caller; on return (stream-ordered) it holds the rotated keys.
+ *             Keys are rotated there by one pass before the attention kernel, which
+ *             re-reads every key once per 128-query tile; queries are rotated in
+ *             registers as they are loaded.  Ignored (may be NULL) without tables.
+ * out, lse    as for pfa_varlen_fwd (out 16-byte aligned).
+ * cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale, stream: as for pfa_varlen_fwd.
+ * Errors: as for pfa_varlen_fwd, plus PFA_ERR_NULL for one table without the other or
+ * tables without k_rot, PFA_ERR_ALIAS when out, lse or k_rot is an input or two of them
+ * coincide, PFA_ERR_ALIGN, and PFA_ERR_SIZE when 3 * heads * head_dim exceeds 2^23.
+ */
+PFA_API int pfa_varlen_fwd_qkv(const void* qkv, const float* rope_cos, const float* rope_sin,
+                               const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                               int heads, int head_dim, float scale, void* out, float* lse,
+                               void* k_rot, hipStream_t stream);
 
 /*
  * pfa_attn_merge -- combine two results for the same queries over disjoint key sets.

@@ -14,7 +14,8 @@ import numpy as np
 
 from . import _lib
 
-__all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_bwd", "pfa_attn_merge",
+__all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv", "pfa_varlen_bwd",
+           "pfa_attn_merge",
            "pfa_check_cu_seqlens",
            "pfa_status_string", "PfaError", "LIB_PATH"]
 
@@ -134,6 +135,60 @@ def pfa_varlen_fwd_qk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
     if rc != 0:
         raise PfaError(rc)
     return out, lse
+
+
+def pfa_varlen_fwd_qkv(qkv, cu_seqlens, max_seqlen: int, scale: float | None = None,
+                       rope_cos=None, rope_sin=None, out=None, lse=None, want_lse: bool = True,
+                       k_rot=None, stream=None):
+    """Self-attention forward read straight from a fused projection output.
+
+    qkv: contiguous bf16 CUDA tensor [T, 3, H, d] (a [T, 3 * H * d] projection output
+    viewed as such).  rope_cos, rope_sin: contiguous fp32 CUDA
+    tensors [T, d / 2], or both None for no rotation; with them, q and k are rotated
+    (rotate-half pairs) before attention and the rotated keys land in ``k_rot``
+    ([T, H, d] bf16, allocated when not given).  Returns (out [T, H, d] bf16, lse [H, T]
+    fp32 or None, k_rot or None)."""
+    import torch
+
+    if (not qkv.is_cuda or qkv.dtype != torch.bfloat16 or not qkv.is_contiguous() or qkv.dim() != 4
+            or qkv.shape[1] != 3):
+        raise ValueError("qkv must be a contiguous bf16 CUDA tensor [T, 3, H, d]")
+    _check_table("cu_seqlens", cu_seqlens, torch)
+    T, _, H, d = qkv.shape
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("pass both rope_cos and rope_sin, or neither")
+    if rope_cos is not None:
+        for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            if (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
+                    or tuple(t.shape) != (T, d // 2)):
+                raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor [T, d/2]")
+        if k_rot is None:
+            k_rot = torch.empty((T, H, d), dtype=torch.bfloat16, device=qkv.device)
+        else:
+            _check_bf16("k_rot", k_rot, torch)
+            if tuple(k_rot.shape) != (T, H, d):
+                raise ValueError("k_rot must be [T, H, d]")
+    else:
+        k_rot = None
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((T, H, d), dtype=torch.bfloat16, device=qkv.device)
+    elif tuple(out.shape) != (T, H, d) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor [T, H, d]")
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=qkv.device)
+    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device)
+    rc = _lib.load().pfa_varlen_fwd_qkv(
+        _ptr(qkv), _ptr(rope_cos), _ptr(rope_sin), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        int(max_seqlen), H, d, float(scale), _ptr(out), _ptr(lse), _ptr(k_rot),
+        ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse, k_rot
 
 
 def pfa_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, want_lse: bool = True,

@@ -17,6 +17,8 @@ _SIGNATURES = {
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]),
+    "pfa_varlen_fwd_qkv": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
+                           [ctypes.c_float] + [ctypes.c_void_p] * 4),
     "pfa_attn_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),

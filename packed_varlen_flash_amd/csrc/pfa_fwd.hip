@@ -73,7 +73,22 @@ struct Params {
   int heads;
   int qt_max;      // ceil(max_seqlen / BM): slots per (segment, head) in unsorted mode
   float c;         // scale * log2(e)
+  // fused-projection variant only: row strides (elements) of q, k, v, and the rotary
+  // angle tables [T, D/2] applied to q as it is loaded (nullptr: no rotation)
+  int sq, sk, sv;
+  const float* rope_cos;
+  const float* rope_sin;
 };
+
+// Kernel variants: one segment table for queries and keys; separate query and key tables;
+// one table with q, k, v read through row strides (views of one fused projection output)
+// and q optionally rotated on load.
+constexpr int kModeSelf = 0;
+constexpr int kModeCross = 1;
+constexpr int kModeQkv = 2;
+// Largest row stride (elements) of any input: 64 rows of it, in bytes, must stay within
+// the 32-bit offsets of a buffer resource.
+constexpr int64_t kMaxRowElems = int64_t(1) << 23;
 
 // D: head_dim; QB: 32-query blocks per wave; NW: waves per workgroup; SK: keys per LDS
 // stage (a multiple of 64).
@@ -380,9 +395,35 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
   }
 }
 
-// CROSS only keys the instantiation to its kernel variant (the HIP host pass rejects a
+// Rotary position embedding, rotate-half pairing, of one pair of 8-feature chunks: lo
+// holds features i .. i+7 of a row and hi their partners i + D/2 .. i + D/2 + 7; cs and
+// sn point at the cosines and sines of those 8 pairs' angles.  Each pair (a, b) turns to
+// (a cos - b sin, b cos + a sin), evaluated in fp32 and rounded once to bf16 (nearest
+// even).  The DiT block of the Mage-Flow page (section on its fusion opportunities)
+// rotates q and k between the QKV projection and attention.
+__device__ __forceinline__ void rope_rotate(bf16x8& lo, bf16x8& hi, const float* cs, const float* sn) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
+  const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(sn);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(sn + 4);
+  bf16x8 nlo, nhi;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c = e < 4 ? c0[e & 3] : c1[e & 3];
+    const float sv = e < 4 ? s0[e & 3] : s1[e & 3];
+    const float a = (float)lo[e];
+    const float b = (float)hi[e];
+    nlo[e] = (__bf16)(a * c - b * sv);
+    nhi[e] = (__bf16)(b * c + a * sv);
+  }
+  lo = nlo;
+  hi = nhi;
+}
+
+// MODE also keys the instantiation to its kernel variant (the HIP host pass rejects a
 // device template specialisation shared by two kernel templates' instantiations).
-template <int D, int QB, int NW, int SK, bool CROSS>
+template <int D, int QB, int NW, int SK, int MODE>
 __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int qa,
                                              int Lq, int ka, int Lk, int h, int qt, int Tq) {
   using C = Tile<D, QB, NW, SK>;
@@ -393,11 +434,14 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const int g = lane >> 5;           // half-wave
   const int i16 = lane & 15;
   const int hh = (lane >> 4) & 1;
-  const int64_t rs = (int64_t)p.heads * D;  // elements between consecutive tokens
+  const int64_t rs = (int64_t)p.heads * D;  // elements between consecutive output tokens
+  const int64_t q_rs = MODE == kModeQkv ? (int64_t)p.sq : rs;   // ... and input tokens
+  const int64_t k_rs = MODE == kModeQkv ? (int64_t)p.sk : rs;
+  const int64_t v_rs = MODE == kModeQkv ? (int64_t)p.sv : rs;
   const int64_t head_off = (int64_t)h * D;
-  const __bf16* qbase = p.q + (int64_t)qa * rs + head_off;
-  const __bf16* kbase = p.k + (int64_t)ka * rs + head_off;
-  const __bf16* vbase = p.v + (int64_t)ka * rs + head_off;
+  const __bf16* qbase = p.q + (int64_t)qa * q_rs + head_off;
+  const __bf16* kbase = p.k + (int64_t)ka * k_rs + head_off;
+  const __bf16* vbase = p.v + (int64_t)ka * v_rs + head_off;
   const int q0 = qt * C::BM + wave * (QB * 32);
   const int ns = (Lk + SK - 1) / SK;       // LDS stages (0 when the key segment is empty)
   const float c = p.c;
@@ -409,8 +453,19 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
     for (int t = 0; t < C::KSTEP; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < Lq) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * rs + 16 * t + 8 * g);
+      if (row < Lq) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * q_rs + 16 * t + 8 * g);
       st.qr[b][t] = __builtin_bit_cast(bf16x8, x);
+    }
+    if constexpr (MODE == kModeQkv) {
+      // rotate-half RoPE: the lane's chunk t holds features 16t + 8g + 0..7 and chunk
+      // t + KSTEP/2 their partners D/2 further on, so each pair is rotated in registers
+      if (p.rope_cos != nullptr && row < Lq) {
+        const int64_t tab = (int64_t)(qa + row) * (D / 2);
+#pragma unroll
+        for (int t = 0; t < C::KSTEP / 2; ++t)
+          rope_rotate(st.qr[b][t], st.qr[b][t + C::KSTEP / 2], p.rope_cos + tab + 16 * t + 8 * g,
+                      p.rope_sin + tab + 16 * t + 8 * g);
+      }
     }
     st.m_run[b] = -INFINITY;
     st.l_run[b] = 0.f;
@@ -433,24 +488,25 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   // load writes physical chunk (wave*CPT + i)*64 + l, fetched from its logical source.
   // A buffer resource bounded at the segment end returns zeros for rows >= L, so no row
   // of a neighbouring segment is ever read.
-  const int row_bytes = (int)(rs * 2);   // the host keeps 64 rows within int range
+  // the host keeps 64 rows of every stride within int range
+  const int kbytes = (int)(k_rs * 2);
+  const int vbytes = (int)(v_rs * 2);
   char* const kring = reinterpret_cast<char*>(ks);
   char* const vring = reinterpret_cast<char*>(vs);
   int src_k[C::CPT], src_v[C::CPT];      // logical source offsets of this lane's chunks
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
     const int P = (wave * C::CPT + i) * 64 + lane;
-    src_k[i] = logical_src<D, true>(P, row_bytes);
-    src_v[i] = logical_src<D, false>(P, row_bytes);
+    src_k[i] = logical_src<D, true>(P, kbytes);
+    src_v[i] = logical_src<D, false>(P, vbytes);
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
     const int kb = stage * SK;
     const int rows = (Lk - kb < SK) ? (Lk - kb) : SK;
-    const int nrec = rows * row_bytes;
     __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * k_rs), 0, rows * kbytes, kRsrcFlags);
     __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * rs), 0, nrec, kRsrcFlags);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * v_rs), 0, rows * vbytes, kRsrcFlags);
     kdst += wave * C::CPT * 1024;
     vdst += wave * C::CPT * 1024;
 #pragma unroll
@@ -520,12 +576,12 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   __syncthreads();   // the next tile's first stage overwrites the ring
 }
 
-// CROSS: separate query and key tables; otherwise the key table is the query table
+// kModeCross: separate query and key tables; otherwise the key table is the query table
 // (known at compile time, so the key-side offsets and lengths fold into the query ones).
-template <int D, int QB, int NW, int SK, int WPE, bool CROSS>
+template <int D, int QB, int NW, int SK, int WPE, int MODE>
 __global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 pfa_fwd_kernel(Params p) {
-  const int32_t* const cu_k = CROSS ? p.cu_k : p.cu_q;
+  const int32_t* const cu_k = MODE == kModeCross ? p.cu_k : p.cu_q;
   using C = Tile<D, QB, NW, SK>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
@@ -580,14 +636,57 @@ pfa_fwd_kernel(Params p) {
     if (Lq > Tq - qa) Lq = Tq - qa;
     if (Lq <= 0 || qt * C::BM >= Lq) continue;
     int ka = qa, Lk = Lq;
-    if (CROSS) {
+    if (MODE == kModeCross) {
       ka = cu_k[s];
       Lk = cu_k[s + 1] - ka;
       if (ka < 0 || ka > Tk) ka = Tk;
       if (Lk > Tk - ka) Lk = Tk - ka;
       if (Lk < 0) Lk = 0;
     }
-    process_tile<D, QB, NW, SK, CROSS>(p, ks, vs, qa, Lq, ka, Lk, h, qt, Tq);
+    process_tile<D, QB, NW, SK, MODE>(p, ks, vs, qa, Lq, ka, Lk, h, qt, Tq);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Key rotation pass of the fused-projection forward: k_rot[t, h, :] = RoPE(k[t, h, :])
+// with token t's angles, written contiguous [T, heads, D].  The forward kernel re-reads
+// every key stage once per query tile of its segment, so the keys are rotated once here
+// rather than at each load; queries are rotated in registers where they are loaded.
+// One thread per pair of 16-byte chunks (features 8j .. 8j+7 and their partners D/2
+// further on); consecutive threads cover consecutive chunks, then heads, then tokens,
+// so a wave reads and writes whole contiguous rows.  HBM-bound.
+// ---------------------------------------------------------------------------------
+constexpr int kRopeThreads = 256;
+
+struct RopeParams {
+  const __bf16* src;     // row t, head h at src + t * stride + h * D
+  __bf16* dst;           // [T, heads, D]
+  const float* cos;      // [T, D/2]
+  const float* sin;
+  const int32_t* cu;     // T = cu[num_seqs], read on the device
+  int num_seqs;
+  int heads;
+  int stride;
+};
+
+template <int D>
+__global__ void __launch_bounds__(kRopeThreads) pfa_rope_k_kernel(RopeParams r) {
+  constexpr int CPH = D / 16;                  // chunk pairs per (token, head) row
+  const int64_t T = r.cu[r.num_seqs];
+  const int64_t n = T * r.heads * CPH;         // <= 0 for a table that ends below zero
+  for (int64_t idx = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * kRopeThreads) {
+    const int64_t row = idx / CPH;
+    const int j = (int)(idx - row * CPH);
+    const int64_t t = row / r.heads;
+    const int h = (int)(row - t * r.heads);
+    const __bf16* src = r.src + t * r.stride + (int64_t)h * D + 8 * j;
+    bf16x8 lo = *reinterpret_cast<const bf16x8*>(src);
+    bf16x8 hi = *reinterpret_cast<const bf16x8*>(src + D / 2);
+    rope_rotate(lo, hi, r.cos + t * (D / 2) + 8 * j, r.sin + t * (D / 2) + 8 * j);
+    __bf16* dst = r.dst + row * D + 8 * j;
+    *reinterpret_cast<bf16x8*>(dst) = lo;
+    *reinterpret_cast<bf16x8*>(dst + D / 2) = hi;
   }
 }
 
@@ -1137,20 +1236,20 @@ struct Variant {
   size_t lds;
 };
 
-template <int D, int QB, int NW, int SK, int WPE, bool CROSS>
+template <int D, int QB, int NW, int SK, int WPE, int MODE>
 Variant make_variant() {
   using C = Tile<D, QB, NW, SK>;
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, CROSS>), C::BM,
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, MODE>), C::BM,
                  C::THREADS, C::LDS_BYTES};
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 4;  // head_dim 64, 128; one table or separate q / k tables
+constexpr int kVariants = 6;  // head_dim 64, 128 x the three kernel modes
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 std::atomic<int> g_bwd_occ[kMaxDevices][2][2];   // [device][head_dim 64 / 128][dK-dV / dQ]
 
-int variant_index(int head_dim, bool cross) { return (head_dim == 64 ? 0 : 1) + (cross ? 2 : 0); }
+int variant_index(int head_dim, int mode) { return (head_dim == 64 ? 0 : 1) + 2 * mode; }
 
 #ifndef PFA_D64_QB
 #define PFA_D64_QB 2
@@ -1177,13 +1276,64 @@ int variant_index(int head_dim, bool cross) { return (head_dim == 64 ? 0 : 1) + 
 #define PFA_D128_SK 64
 #endif
 
-Variant variant_for(int head_dim, bool cross) {
-  if (head_dim == 64)
-    return cross ? make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, true>()
-                 : make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, false>();
-  return cross ? make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, true>()
-               : make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, false>();
+template <int MODE>
+Variant variant_of(int head_dim) {
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, MODE>();
+  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, MODE>();
 }
+
+Variant variant_for(int head_dim, int mode) {
+  return mode == kModeCross ? variant_of<kModeCross>(head_dim)
+       : mode == kModeQkv   ? variant_of<kModeQkv>(head_dim)
+                            : variant_of<kModeSelf>(head_dim);
+}
+
+// compute units of the current device (cached; a race only recomputes the same value)
+int device_cus(int* dev_out, int* cus_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_DEVICE;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return PFA_ERR_DEVICE;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  *dev_out = dev;
+  *cus_out = cus;
+  return PFA_OK;
+}
+
+// Size the persistent grid of one forward variant and launch it.  prm carries every
+// field but qt_max; the caller has checked the arguments.
+int launch_fwd(Params prm, int mode, int max_seqlen_q, int head_dim, hipStream_t stream) {
+  const Variant var = variant_for(head_dim, mode);
+  const int64_t qt_max = ((int64_t)max_seqlen_q + var.bm - 1) / var.bm;
+  const int64_t slots = (int64_t)prm.num_seqs * prm.heads * qt_max;
+  if (slots > INT32_MAX) return PFA_ERR_SIZE;
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != PFA_OK) return rc;
+  const int vi = variant_index(head_dim, mode);
+  int occ = g_occ[dev][vi].load(std::memory_order_relaxed);
+  if (occ <= 0) {
+    if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)var.lds) != hipSuccess)
+      return PFA_ERR_DEVICE;
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, var.threads, var.lds) != hipSuccess || o <= 0)
+      return PFA_ERR_DEVICE;
+    occ = o;
+    g_occ[dev][vi].store(occ, std::memory_order_relaxed);
+  }
+  int64_t grid = (int64_t)cus * occ;
+  if (grid > slots) grid = slots;
+  if (grid >= 8) grid -= grid % 8;   // keep whole rounds on every XCD
+  prm.qt_max = (int)qt_max;
+  void* args[] = {&prm};
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, var.lds, stream);
+  return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
+}
+
+bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
 
 }  // namespace
 
@@ -1203,6 +1353,7 @@ PFA_API const char* pfa_status_string(int status) {
     case PFA_ERR_DEVICE: return "no usable HIP device, or a device query failed";
     case PFA_ERR_LAUNCH: return "kernel launch failed";
     case PFA_ERR_SIZE: return "problem size exceeds the supported index range";
+    case PFA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
     default: return "unknown status";
   }
 }
@@ -1238,38 +1389,9 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const
   for (const void* in : ins)
     if (in == out || (lse != nullptr && in == static_cast<const void*>(lse))) return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
-  const bool cross = cu_seqlens_k != cu_seqlens_q;
-  const Variant var = variant_for(head_dim, cross);
-  const int64_t qt_max = ((int64_t)max_seqlen_q + var.bm - 1) / var.bm;
-  const int64_t slots = (int64_t)num_seqs * heads * qt_max;
-  if ((int64_t)heads * head_dim > INT32_MAX || slots > INT32_MAX) return PFA_ERR_SIZE;
+  if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
 
-  // ---- device limits (cached per device; a race only recomputes the same values)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_DEVICE;
-  int cus = g_cus[dev].load(std::memory_order_relaxed);
-  if (cus <= 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return PFA_ERR_DEVICE;
-    g_cus[dev].store(cus, std::memory_order_relaxed);
-  }
-  const int vi = variant_index(head_dim, cross);
-  int occ = g_occ[dev][vi].load(std::memory_order_relaxed);
-  if (occ <= 0) {
-    if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)var.lds) != hipSuccess)
-      return PFA_ERR_DEVICE;
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, var.threads, var.lds) != hipSuccess || o <= 0)
-      return PFA_ERR_DEVICE;
-    occ = o;
-    g_occ[dev][vi].store(occ, std::memory_order_relaxed);
-  }
-
-  int64_t grid = (int64_t)cus * occ;
-  if (grid > slots) grid = slots;
-  if (grid >= 8) grid -= grid % 8;   // keep whole rounds on every XCD
-
-  Params prm;
+  Params prm{};
   prm.q = static_cast<const __bf16*>(q);
   prm.k = static_cast<const __bf16*>(k);
   prm.v = static_cast<const __bf16*>(v);
@@ -1279,11 +1401,9 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const
   prm.lse = lse;
   prm.num_seqs = num_seqs;
   prm.heads = heads;
-  prm.qt_max = (int)qt_max;
   prm.c = scale * kLog2e;
-  void* args[] = {&prm};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, var.lds, stream);
-  return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
+  const int mode = cu_seqlens_k != cu_seqlens_q ? kModeCross : kModeSelf;
+  return launch_fwd(prm, mode, max_seqlen_q, head_dim, stream);
 }
 
 PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
@@ -1291,6 +1411,75 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
                            void* out, float* lse, hipStream_t stream) {
   return pfa_varlen_fwd_qk(q, k, v, cu_seqlens, cu_seqlens, num_seqs, max_seqlen, max_seqlen, heads,
                            head_dim, scale, out, lse, stream);
+}
+
+PFA_API int pfa_varlen_fwd_qkv(const void* qkv, const float* rope_cos, const float* rope_sin,
+                               const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
+                               int head_dim, float scale, void* out, float* lse, void* k_rot,
+                               hipStream_t stream) {
+  // ---- argument checks: all before any HIP runtime call
+  if (qkv == nullptr || cu_seqlens == nullptr || out == nullptr) return PFA_ERR_NULL;
+  const bool rope = rope_cos != nullptr || rope_sin != nullptr;
+  if (rope && (rope_cos == nullptr || rope_sin == nullptr || k_rot == nullptr)) return PFA_ERR_NULL;
+  if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (max_seqlen < 1) return PFA_ERR_MAX_SEQLEN;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
+  const void* ins[4] = {qkv, cu_seqlens, rope_cos, rope_sin};
+  const void* outs[3] = {out, lse, rope ? k_rot : nullptr};
+  for (int a = 0; a < 3; ++a) {
+    if (outs[a] == nullptr) continue;
+    for (const void* in : ins)
+      if (in == outs[a]) return PFA_ERR_ALIAS;
+    for (int b = a + 1; b < 3; ++b)
+      if (outs[a] == outs[b]) return PFA_ERR_ALIAS;
+  }
+  if (misaligned16(qkv) || misaligned16(out) ||
+      (rope && (misaligned16(k_rot) || misaligned16(rope_cos) || misaligned16(rope_sin))))
+    return PFA_ERR_ALIGN;
+  const int64_t hd = (int64_t)heads * head_dim;
+  if (3 * hd > kMaxRowElems) return PFA_ERR_SIZE;
+  const int bm = variant_for(head_dim, kModeQkv).bm;   // launch_fwd repeats this check
+  if ((int64_t)num_seqs * heads * (((int64_t)max_seqlen + bm - 1) / bm) > INT32_MAX) return PFA_ERR_SIZE;
+
+  const __bf16* base = static_cast<const __bf16*>(qkv);
+  Params prm{};
+  prm.q = base;
+  prm.k = rope ? static_cast<const __bf16*>(k_rot) : base + hd;
+  prm.v = base + 2 * hd;
+  prm.cu_q = cu_seqlens;
+  prm.cu_k = cu_seqlens;
+  prm.out = static_cast<__bf16*>(out);
+  prm.lse = lse;
+  prm.num_seqs = num_seqs;
+  prm.heads = heads;
+  prm.c = scale * kLog2e;
+  prm.sq = (int)(3 * hd);
+  prm.sk = (int)(rope ? hd : 3 * hd);
+  prm.sv = (int)(3 * hd);
+  prm.rope_cos = rope_cos;
+  prm.rope_sin = rope_sin;
+  if (rope) {
+    int dev = 0, cus = 0;
+    const int rc = device_cus(&dev, &cus);
+    if (rc != PFA_OK) return rc;
+    RopeParams rp;
+    rp.src = base + hd;
+    rp.dst = static_cast<__bf16*>(k_rot);
+    rp.cos = rope_cos;
+    rp.sin = rope_sin;
+    rp.cu = cu_seqlens;
+    rp.num_seqs = num_seqs;
+    rp.heads = heads;
+    rp.stride = (int)(3 * hd);
+    void* args[] = {&rp};
+    const void* fn = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_rope_k_kernel<64>)
+                                    : reinterpret_cast<const void*>(&pfa_rope_k_kernel<128>);
+    if (hipLaunchKernel(fn, dim3((unsigned)cus * 8), dim3(kRopeThreads), args, 0, stream) != hipSuccess)
+      return PFA_ERR_LAUNCH;
+  }
+  return launch_fwd(prm, kModeQkv, max_seqlen, head_dim, stream);
 }
 
 PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
@@ -1317,16 +1506,11 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
   }
   const int64_t tiles_max = ((int64_t)max_seqlen + kBwdRows - 1) / kBwdRows;
   const int64_t slots = (int64_t)num_seqs * heads * tiles_max;
-  if ((int64_t)heads * head_dim > INT32_MAX || slots > INT32_MAX) return PFA_ERR_SIZE;
+  if ((int64_t)heads * head_dim > kMaxRowElems || slots > INT32_MAX) return PFA_ERR_SIZE;
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_DEVICE;
-  int cus = g_cus[dev].load(std::memory_order_relaxed);
-  if (cus <= 0) {
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      return PFA_ERR_DEVICE;
-    g_cus[dev].store(cus, std::memory_order_relaxed);
-  }
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != PFA_OK) return rc;
   const void* prep = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_prep_kernel<64>)
                                     : reinterpret_cast<const void*>(&pfa_bwd_prep_kernel<128>);
   const void* dkdv = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_dkdv_kernel<64>)

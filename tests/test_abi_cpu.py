@@ -26,9 +26,9 @@ def declared_symbols():
 
 
 def test_header_declares_the_abi():
-    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_bwd",
-                                       "pfa_attn_merge", "pfa_check_cu_seqlens",
-                                       "pfa_status_string"}
+    assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv",
+                                       "pfa_varlen_bwd", "pfa_attn_merge",
+                                       "pfa_check_cu_seqlens", "pfa_status_string"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-11, 1):
+    for code in range(-12, 1):
         assert lib.pfa_status_string(code)
     assert lib.pfa_status_string(-999) == b"unknown status"
 
@@ -65,6 +65,7 @@ def test_argument_checks_run_before_any_hip_call(lib):
     assert _fwd(lib, lse=2) == -7
     assert _fwd(lib, lse=5) == -7
     assert _fwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
+    assert _fwd(lib, heads=2**17 + 1, head_dim=64) == -11     # a row over 2^23 elements
 
 
 def _fwd_qk(lib, q=1, k=2, v=3, cu_q=4, cu_k=8, num_seqs=1, max_q=1, max_k=1, heads=1,
@@ -86,6 +87,36 @@ def test_qk_argument_checks_run_before_any_hip_call(lib):
     assert _fwd_qk(lib, lse=8) == -7
     assert _fwd_qk(lib, lse=5) == -7
     assert _fwd_qk(lib, num_seqs=2**30, heads=2**10, max_q=2**20) == -11
+
+
+def _qkv(lib, qkv=16, cos=32, sin=48, cu=64, num_seqs=1, max_seqlen=1, heads=1, head_dim=64,
+         scale=1.0, out=80, lse=96, k_rot=112):
+    return lib.pfa_varlen_fwd_qkv(qkv, cos, sin, cu, num_seqs, max_seqlen, heads, head_dim, scale,
+                                  out, lse, k_rot, None)
+
+
+def test_qkv_argument_checks_run_before_any_hip_call(lib):
+    assert _qkv(lib, qkv=None) == -1
+    assert _qkv(lib, cu=None) == -1
+    assert _qkv(lib, out=None) == -1
+    assert _qkv(lib, cos=None) == -1            # one table without the other
+    assert _qkv(lib, sin=None) == -1
+    assert _qkv(lib, k_rot=None) == -1          # tables need the key workspace
+    assert _qkv(lib, num_seqs=0) == -2
+    assert _qkv(lib, heads=0) == -3
+    assert _qkv(lib, max_seqlen=0) == -4
+    assert _qkv(lib, head_dim=96) == -5
+    assert _qkv(lib, scale=float("inf")) == -6
+    assert _qkv(lib, out=16) == -7              # out is the fused input
+    assert _qkv(lib, k_rot=32) == -7            # workspace is a table
+    assert _qkv(lib, lse=80) == -7              # two outputs share a buffer
+    assert _qkv(lib, k_rot=96) == -7
+    assert _qkv(lib, qkv=18) == -12
+    assert _qkv(lib, out=88) == -12
+    assert _qkv(lib, k_rot=120) == -12
+    assert _qkv(lib, sin=52) == -12
+    assert _qkv(lib, heads=2**16, head_dim=64) == -11      # 3 * H * d over 2^23
+    assert _qkv(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
 
 
 def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):
