@@ -22,6 +22,9 @@ marshals:
 * ``qkv_rope_fwd(qkv, cu_seqlens, scale, cos=None, sin=None, rows=None)``: attention on a
   fused ``[T, 3, H, d]`` bf16 projection output, with q and k rotated and rounded to bf16
   first when tables are given.
+* ``varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale, layout, block_q, block_k, rows)``:
+  restricted attention over listed key blocks per (segment, head, query block), numpy
+  fp64; ``block_lists_from_mask`` turns a token mask into such lists.
 * ``widen_bf16(bits)`` / ``round_bf16_bits(x)``: bf16 bits to fp64 and back (one
   rounding, ties to even).
 * ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
@@ -228,6 +231,89 @@ def round_bf16_bits(x):
     m, e = np.frexp(np.asarray(x, dtype=np.float64))
     r = np.ldexp(np.rint(m * 256.0), e - 8).astype(np.float32)
     return (r.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def block_lists_from_mask(mask, block_q: int, block_k: int):
+    """Block layout of a boolean token mask [n, n] (True = the pair is allowed): query block
+    I lists key block J when any pair of the two blocks is allowed, the accounting of the
+    SparseAttn article (section 04: a block with one allowed pair is computed whole).
+    Returns (lists, stats): lists[I] = ascending key block indices; stats = allowed pairs,
+    active blocks, computed positions (active blocks times block area) and utilisation."""
+    m = np.asarray(mask, dtype=bool)
+    n = m.shape[0]
+    nq, nk = -(-n // block_q), -(-m.shape[1] // block_k)
+    lists, active, computed = [], 0, 0
+    for I in range(nq):
+        rows = m[I * block_q:(I + 1) * block_q]
+        row_list = []
+        for J in range(nk):
+            blk = rows[:, J * block_k:(J + 1) * block_k]
+            if blk.any():
+                row_list.append(J)
+                active += 1
+                computed += blk.size
+        lists.append(row_list)
+    pairs = int(m.sum())
+    return lists, {"pairs": pairs, "active_blocks": active, "computed": computed,
+                   "utilisation": pairs / computed if computed else 0.0}
+
+
+def varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale: float, layout, block_q: int = 256,
+                           block_k: int = 64, rows=None):
+    """Block-sparse restricted attention inside each segment.
+
+    Query i of segment s (rows [a, a + L)) belongs to query block (i - a) // block_q; it
+    attends exactly the keys j of its own segment whose key block (j - a) // block_k is
+    listed for its (segment, head, query block), and the softmax is renormalised over
+    that retained set (SparseAttn article, section 3.1: the restricted softmax; its
+    section 05: a sliding-tile layout lets a query tile share a set of key tiles).
+    ``layout[hl][s][qb]`` lists key block indices; ``len(layout)`` is 1 (one layout for
+    every head) or H (head h uses ``layout[h]``).  Indices outside the segment's key
+    blocks are ignored; a repeated index is an error.  A row with no retained key gets
+    O = 0 and LSE = -inf.  Two passes per query block in fp64: exact row maximum, then
+    normaliser and weighted sum; the products are numpy matmuls.  Returns (out, lse) as
+    ``varlen_fwd`` does, for all rows or the sample ``rows``."""
+    def as_f64(a):
+        a = np.asarray(a)
+        return widen_bf16(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float64)
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, _ = q.shape
+    dv = v.shape[2]
+    if len(layout) not in (1, H):
+        raise ValueError("layout must hold one entry or one per head")
+    want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    slot = np.full(T, -1, dtype=np.int64)
+    slot[want] = np.arange(want.shape[0])
+    out = np.zeros((want.shape[0], H, dv))
+    lse = np.full((H, want.shape[0]), -np.inf)
+    for s in range(cu.shape[0] - 1):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        nkb = -(-L // block_k)
+        for qb in range(-(-L // block_q)):
+            r0, r1 = a + qb * block_q, a + min((qb + 1) * block_q, L)
+            dst = slot[r0:r1]
+            if not np.any(dst >= 0):
+                continue
+            for h in range(H):
+                listed = list(layout[h if len(layout) == H else 0][s][qb])
+                if len(set(listed)) != len(listed):
+                    raise ValueError(f"repeated key block in segment {s}, head {h}, query block {qb}")
+                keys = [np.arange(a + J * block_k, a + min((J + 1) * block_k, L))
+                        for J in listed if 0 <= J < nkb]
+                if not keys:
+                    continue                           # O = 0, LSE = -inf
+                kk = np.concatenate(keys)
+                sc = scale * (q[r0:r1, h] @ k[kk, h].T)
+                m = sc.max(axis=1, keepdims=True)
+                w = np.exp(sc - m)
+                z = w.sum(axis=1, keepdims=True)
+                o = (w @ v[kk, h]) / z
+                l = (m + np.log(z))[:, 0]
+                sel = dst >= 0
+                out[dst[sel], h] = o[sel]
+                lse[h, dst[sel]] = l[sel]
+    return out, lse
 
 
 def merge(o_a, lse_a, o_b, lse_b):

@@ -261,6 +261,62 @@ def fuse_qkv(q, k, v) -> np.ndarray:
     return np.ascontiguousarray(np.stack([q, k, v], axis=1))
 
 
+# ---------------------------------------------------------- block-sparse tile layouts
+
+SPARSE_BLOCK_Q = 256    # query rows per listed block (one query tile of the kernel)
+SPARSE_BLOCK_K = 64     # keys per key block
+
+
+def band_layout(lengths, radius: int, block_q: int = SPARSE_BLOCK_Q,
+                block_k: int = SPARSE_BLOCK_K) -> list:
+    """A sliding-tile band: query block I of a segment lists every key block that overlaps
+    [I*block_q - radius, (I+1)*block_q + radius) inside the segment.  For an image in raster
+    order at 64 patches per row, radius 1024 is a band of +-16 patch rows around the
+    query tile's 4 rows.  Returns layout[0][s][I] (one layout shared by every head)."""
+    segs = []
+    for L in lengths:
+        L = int(L)
+        nkb = -(-L // block_k)
+        rows = []
+        for I in range(-(-L // block_q)):
+            lo = max(0, I * block_q - radius)
+            hi = min(L, (I + 1) * block_q + radius)
+            rows.append(list(range(lo // block_k, min(nkb, -(-hi // block_k)))))
+        segs.append(rows)
+    return [segs]
+
+
+def random_layout(rng: np.random.Generator, lengths, heads_layout: int, density: float,
+                  block_q: int = SPARSE_BLOCK_Q, block_k: int = SPARSE_BLOCK_K) -> list:
+    """Each key block of a segment is listed for a query block with probability
+    ``density``, in a random order; layout[hl][s][I] for hl < heads_layout."""
+    lay = []
+    for _ in range(heads_layout):
+        segs = []
+        for L in lengths:
+            nkb = -(-int(L) // block_k)
+            segs.append([[int(J) for J in rng.permutation(nkb) if rng.random() < density]
+                         for _ in range(-(-int(L) // block_q))])
+        lay.append(segs)
+    return lay
+
+
+def layout_pairs(layout, lengths, heads: int, block_q: int = SPARSE_BLOCK_Q,
+                 block_k: int = SPARSE_BLOCK_K) -> int:
+    """Allowed (query, key) pairs summed over heads: the work a block-sparse pass must do
+    (rows of each query block times keys of each listed block, clipped to the segment)."""
+    total = 0
+    for h in range(heads):
+        hl = layout[h if len(layout) == heads else 0]
+        for s, L in enumerate(lengths):
+            L = int(L)
+            for I, row in enumerate(hl[s]):
+                nq = min(block_q, L - I * block_q)
+                nk = sum(min(block_k, L - J * block_k) for J in set(row) if 0 <= J * block_k < L)
+                total += nq * nk
+    return total
+
+
 def sample_rows(cu_seqlens, stride: int = 61, edge: int = 128, full_upto: int = 4096) -> np.ndarray:
     """Deterministic row sample for configurations too large for the oracle in full.
 

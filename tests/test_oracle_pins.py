@@ -648,3 +648,123 @@ def test_fused_qkv_rope_rounds_rotated_q_and_k_to_bf16():
     assert 0 < diff < 2e-2      # only the bf16 rounding of the rotated q and k separates them
     with pytest.raises(ValueError):
         oracle.qkv_rope_fwd(W.fuse_qkv(w.q, w.k, w.v), w.cu_seqlens, w.scale, cos, None)
+
+
+# ------------------------------------------------------------- block-sparse tile lists
+# SparseAttn article: section 3.1 (softmax restricted to a retained key set), section 04
+# (block accounting: a block with one allowed pair is computed whole; the printed table),
+# section 05 (sliding tiles: a query tile shares a set of key tiles).
+
+def _frame_position_masks(ex):
+    same_frame = ex.frame[:, None] == ex.frame[None, :]
+    same_pos = ex.pixel[:, None] == ex.pixel[None, :]
+    return same_frame, same_pos
+
+
+def test_block_accounting_of_the_temporal_mask_matches_the_printed_counts():
+    """Section 04: the same-position mask in frame-major order covers 64 active 4x4 blocks
+    (1024 computed positions for 256 allowed pairs, utilisation 0.25); in token-major order
+    16 blocks, 256 positions, utilisation 1."""
+    ex = W.worked_example()
+    _, same_pos = _frame_position_masks(ex)
+    _, st = oracle.block_lists_from_mask(same_pos, 4, 4)
+    assert (st["pairs"], st["active_blocks"], st["computed"]) == (256, 64, 1024)
+    assert st["utilisation"] == 0.25
+    perm = np.argsort(ex.pixel, kind="stable")
+    _, st2 = oracle.block_lists_from_mask(same_pos[np.ix_(perm, perm)], 4, 4)
+    assert (st2["pairs"], st2["active_blocks"], st2["computed"], st2["utilisation"]) == (256, 16, 256, 1.0)
+
+
+@pytest.mark.parametrize("mask_name,block,prefixes", [
+    ("frame", 16, ("spatial_head_same_frame", "temporal_head_same_frame")),
+    ("position", 1, ("spatial_head_same_position", "temporal_head_same_position")),
+])
+def test_blocksparse_reproduces_the_printed_table(worked, mask_name, block, prefixes):
+    """Section 04 table, through block lists instead of packs: the same-frame mask is the
+    diagonal of 16-token blocks; the same-position mask, in frame-major order, needs
+    1-token blocks (every query lists the 4 keys of its position)."""
+    ex = W.worked_example()
+    q = np.ascontiguousarray(ex.q.transpose(1, 0, 2))
+    v = np.ascontiguousarray(np.repeat(ex.v[:, None, :], 2, 1))
+    same_frame, same_pos = _frame_position_masks(ex)
+    lists, _ = oracle.block_lists_from_mask(same_frame if mask_name == "frame" else same_pos,
+                                            block, block)
+    o, l = oracle.varlen_fwd_blocksparse(q, q, v, [0, 64], 1.0 / math.sqrt(20), [[lists]],
+                                         block_q=block, block_k=block)
+    full_o, full_l = worked["full"]
+    for head, prefix in enumerate(prefixes):
+        _check(worked["gold"], prefix + "_retained_mass", float(np.exp(l[head] - full_l[head]).mean()))
+        _check(worked["gold"], prefix + "_mse",
+               float(np.mean((o[:, head, :] - full_o[:, head, :]) ** 2)))
+
+
+def _random_layout(rng, lengths, heads_layout, bq, bk, p=0.4):
+    lay = []
+    for _ in range(heads_layout):
+        segs = []
+        for L in lengths:
+            nkb = -(-L // bk)
+            segs.append([[int(J) for J in rng.permutation(nkb) if rng.random() < p]
+                         for _ in range(-(-L // bq))])
+        lay.append(segs)
+    return lay
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_blocksparse_matches_dense_masked_softmax(seed):
+    """Brute force: a dense T x T score matrix with -inf outside the allowed (same segment,
+    listed block) pairs, softmax in numpy; rows with no allowed key are zero / -inf."""
+    rng = np.random.default_rng(40 + seed)
+    lengths = [int(x) for x in rng.integers(0, 90, size=4)]
+    T, H, d, bq, bk = sum(lengths), 3, 8, 16, 8
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    lay = _random_layout(rng, lengths, H if seed % 2 else 1, bq, bk)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    o, l = oracle.varlen_fwd_blocksparse(q, k, v, cu, 0.4, lay, block_q=bq, block_k=bk)
+    for h in range(H):
+        allowed = np.zeros((T, T), dtype=bool)
+        hl = lay[h if len(lay) == H else 0]
+        for s, L in enumerate(lengths):
+            a = int(cu[s])
+            for i in range(L):
+                for J in hl[s][i // bq]:
+                    allowed[a + i, a + J * bk:a + min((J + 1) * bk, L)] = True
+        sc = np.where(allowed, 0.4 * q[:, h] @ k[:, h].T, -np.inf)
+        has = allowed.any(axis=1)
+        m = np.where(has, sc.max(axis=1), 0.0)
+        w = np.where(allowed, np.exp(sc - m[:, None]), 0.0)
+        z = w.sum(axis=1)
+        ref = np.where(has[:, None], (w @ v[:, h]) / np.where(has, z, 1.0)[:, None], 0.0)
+        np.testing.assert_allclose(o[:, h], ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(l[h][has], (m + np.log(np.where(has, z, 1.0)))[has], rtol=0,
+                                   atol=1e-13)
+        assert np.all(np.isneginf(l[h][~has]))
+
+
+def test_blocksparse_with_every_block_listed_is_dense_attention():
+    w = W.make([300, 1, 0, 517], 2, 64, seed=41)
+    lay = [[[list(range(-(-L // 64))) for _ in range(-(-L // 256))] for L in w.lengths]]
+    o, l = oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, lay)
+    o_ref, l_ref = oracle.varlen_fwd(w.q, w.k, w.v, w.cu_seqlens, w.scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
+
+
+def test_blocksparse_list_order_out_of_range_and_empty_rows():
+    rng = np.random.default_rng(42)
+    w = W.make([700, 90], 2, 64, seed=43)
+    lay = _random_layout(rng, w.lengths, 1, 256, 64, p=0.6)
+    lay[0][0][1] = []                                    # query block with no keys
+    o, l = oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, lay)
+    assert np.all(o[256:512] == 0) and np.all(np.isneginf(l[:, 256:512]))
+    shuffled = [[[list(rng.permutation(r)) + [-1, 99] for r in seg] for seg in lay[0]]]
+    o2, l2 = oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, shuffled)
+    np.testing.assert_allclose(o2, o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l2, l, rtol=0, atol=1e-13)
+    rows = np.array([0, 255, 256, 699, 700, 789])
+    o3, l3 = oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, lay, rows=rows)
+    np.testing.assert_array_equal(o3, o[rows])
+    np.testing.assert_array_equal(l3, l[:, rows])
+    bad = [[[r + r[:1] for r in seg] for seg in lay[0]]]
+    with pytest.raises(ValueError):
+        oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, bad)

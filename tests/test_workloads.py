@@ -59,3 +59,15 @@ def test_grid_positions_and_rope_tables():
     assert np.all(cos[0] == 1) and np.all(sin[0] == 0) and np.all(cos[4096] == 1)
     np.testing.assert_allclose(cos ** 2 + sin ** 2, 1, atol=1e-6)
     assert sin[70, 0] == np.float32(np.sin(1.0)) and sin[70, 32] == np.float32(np.sin(6.0))
+
+
+def test_band_layout_and_pair_count():
+    lay = W.band_layout([4096, 100, 0], radius=1024)
+    rows = lay[0][0]
+    assert len(rows) == 16 and rows[0] == list(range(0, 20)) and rows[8] == list(range(16, 52))
+    assert rows[15] == list(range(44, 64))
+    assert lay[0][1] == [[0, 1]] and lay[0][2] == []
+    full = [[[list(range(64))] * 16]]
+    assert W.layout_pairs(full, [4096], heads=3) == 3 * 4096 * 4096
+    assert W.layout_pairs(lay, [4096, 100, 0], heads=1) == \
+        sum(256 * 64 * len(r) for r in rows) + 100 * 100
