@@ -45,8 +45,18 @@ typedef enum pfa_status {
   PFA_ERR_LAUNCH = -10,       /* the kernel launch reported an error                     */
   PFA_ERR_SIZE = -11,         /* a row (heads * head_dim, 3x that for a fused input) over
                                  2^23 elements, or more than 2^31 - 1 work slots or rows */
-  PFA_ERR_ALIGN = -12         /* a buffer that must be 16-byte aligned is not            */
+  PFA_ERR_ALIGN = -12,        /* a buffer that must be 16-byte aligned is not            */
+  PFA_ERR_LAYOUT = -13        /* block-sparse layout: bad layout_heads or nnz; from the
+                                 host validator also bad row pointers or block indices,
+                                 a repeated block, or a query block with no keys         */
 } pfa_status;
+
+/* Block-sparse layouts list key blocks of PFA_SPARSE_BLOCK_K keys per query block of
+ * PFA_SPARSE_BLOCK_Q rows, both counted from the start of the segment; segments of a
+ * block-sparse call hold at most PFA_SPARSE_MAX_SEQLEN tokens. */
+#define PFA_SPARSE_BLOCK_Q 256
+#define PFA_SPARSE_BLOCK_K 64
+#define PFA_SPARSE_MAX_SEQLEN 65536
 
 /*
  * pfa_varlen_fwd -- packed, non-causal, block-diagonal attention forward.
@@ -149,6 +159,61 @@ PFA_API int pfa_varlen_fwd_qkv(const void* qkv, const float* rope_cos, const flo
                                const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
                                int heads, int head_dim, float scale, void* out, float* lse,
                                void* k_rot, hipStream_t stream);
+
+/*
+ * pfa_varlen_fwd_blocksparse -- the packed self-attention forward restricted to listed
+ * key blocks.
+ *
+ * The SparseAttn article (jefxiong.cn, "AIGC 基本功｜视频稀疏注意力的误差与布局") defines a
+ * sparse row as the softmax restricted to the row's retained key set and renormalised over
+ * it (section 3.1). It notes that a kernel saves work only when it skips whole blocks it
+ * knows in advance (sections 04 and 06), and that sliding-tile attention lets each query
+ * tile share one set of key tiles (section 05). Here the retained set of a query is
+ * chosen at block granularity. Query i of segment s (rows [a, a + L)) lies in query block
+ * (i - a) / PFA_SPARSE_BLOCK_Q. It attends the keys j of its own segment whose key block
+ * (j - a) / PFA_SPARSE_BLOCK_K is listed for (s, its head, its query block):
+ *     O[i,h,:] = sum_{j listed} exp(s_ij - M_i) v[j,h,:] / sum_{j listed} exp(s_ij - M_i),
+ *     LSE[h,i] = M_i + ln sum_{j listed} exp(s_ij - M_i),   M_i = max over the listed keys.
+ * Listed blocks are computed whole and unlisted ones are skipped (never loaded).
+ *
+ * kv_ptr, kv_idx  device int32 CSR of the lists. qt_max = ceil(max_seqlen /
+ *             PFA_SPARSE_BLOCK_Q); row r = (s * layout_heads + hl) * qt_max + qb holds the
+ *             key-block indices kv_idx[kv_ptr[r] .. kv_ptr[r+1]) of segment s, layout head
+ *             hl and query block qb. kv_ptr has num_seqs * layout_heads * qt_max + 1 entries
+ *             and kv_idx has nnz (kv_idx may be NULL when nnz is 0). Rows of query blocks a
+ *             segment does not have are ignored. Indices outside the segment's key blocks
+ *             are skipped. The order of a list is free. A repeated index counts its keys
+ *             twice, and the validator rejects it.
+ * layout_heads 1 (every head uses the same lists, hl = 0) or heads (hl = h).
+ * Everything else as for pfa_varlen_fwd. max_seqlen must not exceed PFA_SPARSE_MAX_SEQLEN
+ * (PFA_ERR_SIZE).
+ *
+ * A query block whose list retains no key has no softmax. Its rows get O = 0 and
+ * LSE = -inf. The article treats such rows as invalid input, and the validator rejects
+ * them. Checked here: NULL pointers, the scalars, layout_heads and nnz (PFA_ERR_LAYOUT),
+ * aliasing of out or lse with an input. The row pointers are clamped to [0, nnz] on the
+ * device, so a malformed table never makes the kernel read outside kv_ptr's rows or
+ * kv_idx's nnz entries.
+ */
+PFA_API int pfa_varlen_fwd_blocksparse(const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                       int heads, int head_dim, float scale,
+                                       const int32_t* kv_ptr, const int32_t* kv_idx, int nnz,
+                                       int layout_heads, void* out, float* lse,
+                                       hipStream_t stream);
+
+/*
+ * pfa_check_block_layout -- host validator for a block-sparse layout (host copies of the
+ * tables). It checks cu_seqlens as pfa_check_cu_seqlens does, then: kv_ptr[0] = 0,
+ * non-decreasing, kv_ptr[rows] = nnz; every index within its segment's key blocks; no
+ * index repeated in a row; no existing query block with an empty list (SparseAttn article,
+ * section 09: rows with no retained key are rejected); and rows of query blocks a segment
+ * does not have are empty. Returns PFA_OK or the first failing code (PFA_ERR_LAYOUT for the
+ * layout itself).
+ */
+PFA_API int pfa_check_block_layout(const int32_t* cu_host, int num_seqs, int max_seqlen,
+                                   int heads, int layout_heads, const int32_t* kv_ptr_host,
+                                   const int32_t* kv_idx_host, int nnz);
 
 /*
  * pfa_attn_merge -- combine two results for the same queries over disjoint key sets.

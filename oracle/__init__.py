@@ -292,9 +292,10 @@ def varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale: float, layout, block_q: i
         nkb = -(-L // block_k)
         for qb in range(-(-L // block_q)):
             r0, r1 = a + qb * block_q, a + min((qb + 1) * block_q, L)
-            dst = slot[r0:r1]
-            if not np.any(dst >= 0):
+            qrows = np.arange(r0, r1)[slot[r0:r1] >= 0]       # the requested rows only
+            if qrows.size == 0:
                 continue
+            dst = slot[qrows]
             for h in range(H):
                 listed = list(layout[h if len(layout) == H else 0][s][qb])
                 if len(set(listed)) != len(listed):
@@ -304,15 +305,12 @@ def varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale: float, layout, block_q: i
                 if not keys:
                     continue                           # O = 0, LSE = -inf
                 kk = np.concatenate(keys)
-                sc = scale * (q[r0:r1, h] @ k[kk, h].T)
+                sc = scale * (q[qrows, h] @ k[kk, h].T)
                 m = sc.max(axis=1, keepdims=True)
                 w = np.exp(sc - m)
                 z = w.sum(axis=1, keepdims=True)
-                o = (w @ v[kk, h]) / z
-                l = (m + np.log(z))[:, 0]
-                sel = dst >= 0
-                out[dst[sel], h] = o[sel]
-                lse[h, dst[sel]] = l[sel]
+                out[dst, h] = (w @ v[kk, h]) / z
+                lse[h, dst] = (m + np.log(z))[:, 0]
     return out, lse
 
 

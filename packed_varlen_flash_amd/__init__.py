@@ -15,11 +15,14 @@ import numpy as np
 from . import _lib
 
 __all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv", "pfa_varlen_bwd",
-           "pfa_attn_merge",
+           "pfa_varlen_fwd_blocksparse", "block_layout_csr", "pfa_check_block_layout",
+           "SPARSE_BLOCK_Q", "SPARSE_BLOCK_K", "pfa_attn_merge",
            "pfa_check_cu_seqlens",
            "pfa_status_string", "PfaError", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
+SPARSE_BLOCK_Q = 256    # PFA_SPARSE_BLOCK_Q: query rows per block of a block-sparse layout
+SPARSE_BLOCK_K = 64     # PFA_SPARSE_BLOCK_K: keys per key block
 
 
 class PfaError(RuntimeError):
@@ -189,6 +192,94 @@ def pfa_varlen_fwd_qkv(qkv, cu_seqlens, max_seqlen: int, scale: float | None = N
     if rc != 0:
         raise PfaError(rc)
     return out, lse, k_rot
+
+
+def block_layout_csr(layout, lengths, max_seqlen: int):
+    """Pack nested lists layout[hl][s][qb] (key-block indices; len(layout) = 1 or heads)
+    into the C ABI's CSR: row (s * layout_heads + hl) * qt_max + qb with qt_max =
+    ceil(max_seqlen / SPARSE_BLOCK_Q).  Returns (kv_ptr, kv_idx, layout_heads) as int32
+    numpy arrays plus the int; rows of query blocks a segment lacks stay empty."""
+    lh = len(layout)
+    qt_max = -(-int(max_seqlen) // SPARSE_BLOCK_Q)
+    n = len(lengths)
+    counts = np.zeros(n * lh * qt_max, dtype=np.int64)
+    idx = []
+    for s in range(n):
+        for hl in range(lh):
+            for qb, row in enumerate(layout[hl][s]):
+                if qb >= qt_max:
+                    raise ValueError("a segment has more query blocks than max_seqlen allows")
+                counts[(s * lh + hl) * qt_max + qb] = len(row)
+    for r in range(n * lh * qt_max):
+        s, rem = divmod(r, lh * qt_max)
+        hl, qb = divmod(rem, qt_max)
+        rows = layout[hl][s]
+        if qb < len(rows):
+            idx.extend(int(j) for j in rows[qb])
+    kv_ptr = np.zeros(counts.shape[0] + 1, dtype=np.int64)
+    kv_ptr[1:] = np.cumsum(counts)
+    if kv_ptr[-1] > np.iinfo(np.int32).max:
+        raise ValueError("too many listed blocks")
+    return kv_ptr.astype(np.int32), np.asarray(idx, dtype=np.int32), lh
+
+
+def pfa_check_block_layout(cu_host, max_seqlen: int, heads: int, layout_heads: int, kv_ptr,
+                           kv_idx) -> None:
+    """Validate host copies of a block-sparse layout; raise PfaError when malformed."""
+    cu = np.ascontiguousarray(np.asarray(cu_host, dtype=np.int32))
+    p = np.ascontiguousarray(np.asarray(kv_ptr, dtype=np.int32))
+    i = np.ascontiguousarray(np.asarray(kv_idx, dtype=np.int32))
+    rows = (cu.shape[0] - 1) * int(layout_heads) * (-(-int(max_seqlen) // SPARSE_BLOCK_Q))
+    if p.shape[0] != rows + 1:
+        raise ValueError(f"kv_ptr must have {rows + 1} entries")
+    rc = _lib.load().pfa_check_block_layout(
+        cu.ctypes.data_as(ctypes.c_void_p), cu.shape[0] - 1, int(max_seqlen), int(heads),
+        int(layout_heads), p.ctypes.data_as(ctypes.c_void_p),
+        i.ctypes.data_as(ctypes.c_void_p) if i.size else None, int(i.shape[0]))
+    if rc != 0:
+        raise PfaError(rc)
+
+
+def pfa_varlen_fwd_blocksparse(q, k, v, cu_seqlens, max_seqlen: int, kv_ptr, kv_idx,
+                               layout_heads: int = 1, scale: float | None = None, out=None,
+                               lse=None, want_lse: bool = True, stream=None):
+    """Packed self-attention restricted to listed key blocks (see include/pfa.h).
+
+    q, k, v: contiguous bf16 CUDA tensors [T, H, d]; kv_ptr, kv_idx: int32 CUDA tensors of
+    the CSR layout (``block_layout_csr``); layout_heads: 1 or H.  Returns (out, lse)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t, torch)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    _check_table("cu_seqlens", cu_seqlens, torch)
+    _check_table("kv_ptr", kv_ptr, torch)
+    if kv_idx.numel() > 0:
+        _check_table("kv_idx", kv_idx, torch)
+    T, H, d = q.shape
+    rows = (cu_seqlens.numel() - 1) * int(layout_heads) * (-(-int(max_seqlen) // SPARSE_BLOCK_Q))
+    if kv_ptr.numel() != rows + 1:
+        raise ValueError(f"kv_ptr must have {rows + 1} entries for this max_seqlen and layout_heads")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_fwd_blocksparse(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), H, d,
+        float(scale), _ptr(kv_ptr), _ptr(kv_idx) if kv_idx.numel() > 0 else None, int(kv_idx.numel()),
+        int(layout_heads), _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse
 
 
 def pfa_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, want_lse: bool = True,

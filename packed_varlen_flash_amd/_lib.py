@@ -19,6 +19,11 @@ _SIGNATURES = {
                                          ctypes.c_void_p]),
     "pfa_varlen_fwd_qkv": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
                            [ctypes.c_float] + [ctypes.c_void_p] * 4),
+    "pfa_varlen_fwd_blocksparse": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_int] * 4 +
+                                   [ctypes.c_float] + [ctypes.c_void_p] * 2 +
+                                   [ctypes.c_int] * 2 + [ctypes.c_void_p] * 3),
+    "pfa_check_block_layout": (ctypes.c_int, [ctypes.c_void_p] + [ctypes.c_int] * 4 +
+                               [ctypes.c_void_p] * 2 + [ctypes.c_int]),
     "pfa_attn_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),

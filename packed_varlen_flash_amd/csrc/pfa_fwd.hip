@@ -31,6 +31,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "pfa.h"
 
@@ -78,6 +79,12 @@ struct Params {
   int sq, sk, sv;
   const float* rope_cos;
   const float* rope_sin;
+  // block-sparse variant only: key-block lists per (segment, layout head, query tile), CSR
+  // row (s * layout_heads + hl) * qt_max + qt, entries kv_idx[kv_ptr[row] .. kv_ptr[row+1])
+  const int32_t* kv_ptr;
+  const int32_t* kv_idx;
+  int nnz;
+  int layout_heads;
 };
 
 // Kernel variants: one segment table for queries and keys; separate query and key tables;
@@ -86,6 +93,11 @@ struct Params {
 constexpr int kModeSelf = 0;
 constexpr int kModeCross = 1;
 constexpr int kModeQkv = 2;
+constexpr int kModeSparse = 3;   // one table; each query tile reads only its listed key blocks
+// Block-sparse variant: a compacted copy of the tile's key-block list lives in LDS after
+// the schedule (count in the last slot), so segments are limited to this many key blocks.
+constexpr int kSparseMaxBlocks = 1024;
+constexpr int kSparseLdsBytes = (kSparseMaxBlocks + 4) * 4;
 // Largest row stride (elements) of any input: 64 rows of it, in bytes, must stay within
 // the 32-bit offsets of a buffer resource.
 constexpr int64_t kMaxRowElems = int64_t(1) << 23;
@@ -356,8 +368,8 @@ __device__ __forceinline__ void interleave_mfma_valu() {
   }
 }
 
-// One 64-key stage: issue the next stage's loads into its slot, then QK, softmax and PV
-// on the current slot.  The four LDS pointers are restrict-qualified: the next slot and
+// One stage of keys kbase .. kbase + SK - 1: issue the next stage's loads into its slot,
+// then QK, softmax and PV on the current slot.  The four LDS pointers are restrict-qualified: the next slot and
 // the current slot never overlap, which lets the compiler keep the current slot's reads
 // from waiting on the next slot's loads.  The straight-line half of each sub-block's
 // softmax shares a basic block with the MFMAs of the neighbouring sub-block (QK of the
@@ -366,14 +378,14 @@ template <int D, int QB, int SK, typename IssueFn>
 __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restrict__ knext,
                                            char* __restrict__ vnext, const char* __restrict__ kcur,
                                            const char* __restrict__ vcur, bool issue,
-                                           const IssueFn& issue_fn, int s, int L,
+                                           const IssueFn& issue_fn, int s, int kbase, int L,
                                            const int (&koff)[D / 16], const int (&voff)[D / 32],
                                            float c, int g) {
   constexpr int NQK = QB * D / 16;   // MFMAs of one sub-block's QK (and of its PV)
   if (issue) issue_fn(knext, vnext, s + 1);
 #pragma unroll
   for (int half = 0; half < SK / kHalf; ++half) {
-    const int key0 = s * SK + half * kHalf;
+    const int key0 = kbase + half * kHalf;     // first key of this half (kbase: of the stage)
     if (half > 0 && key0 >= L) break;            // nothing left in this stage
     const char* kh = kcur + half * kHalf * D * 2;
     const char* vh = vcur + half * kHalf * D * 2;
@@ -424,8 +436,9 @@ __device__ __forceinline__ void rope_rotate(bf16x8& lo, bf16x8& hi, const float*
 // MODE also keys the instantiation to its kernel variant (the HIP host pass rejects a
 // device template specialisation shared by two kernel templates' instantiations).
 template <int D, int QB, int NW, int SK, int MODE>
-__device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int qa,
-                                             int Lq, int ka, int Lk, int h, int qt, int Tq) {
+__device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int* s_blk,
+                                             int seg, int qa, int Lq, int ka, int Lk, int h,
+                                             int qt, int Tq) {
   using C = Tile<D, QB, NW, SK>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,8 +456,41 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const __bf16* kbase = p.k + (int64_t)ka * k_rs + head_off;
   const __bf16* vbase = p.v + (int64_t)ka * v_rs + head_off;
   const int q0 = qt * C::BM + wave * (QB * 32);
-  const int ns = (Lk + SK - 1) / SK;       // LDS stages (0 when the key segment is empty)
+  int ns = (Lk + SK - 1) / SK;             // LDS stages (0 when the key segment is empty)
   const float c = p.c;
+  if constexpr (MODE == kModeSparse) {
+    // The tile's list, compacted by wave 0 into LDS: entries outside the segment's key
+    // blocks are dropped, the rest keep their order.  ns becomes the number kept.  (The
+    // previous tile's last barrier retired every reader of the old list.)
+    static_assert(SK == 64, "key blocks are 64-key stages");
+    if (wave == 0) {
+      const int64_t row = ((int64_t)seg * p.layout_heads + (p.layout_heads == 1 ? 0 : h)) * p.qt_max + qt;
+      int e0 = 0, e1 = 0;
+      if (qt < p.qt_max) {
+        e0 = min(max(p.kv_ptr[row], 0), p.nnz);
+        e1 = min(max(p.kv_ptr[row + 1], e0), p.nnz);
+      }
+      int cnt = 0;
+      for (int base = e0; base < e1; base += kWave) {
+        const int i = base + lane;
+        const int b = i < e1 ? p.kv_idx[i] : -1;
+        const bool ok = b >= 0 && b < ns;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(ok);
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (ok && pos < kSparseMaxBlocks) s_blk[pos] = b;
+        cnt += __builtin_popcountll(m);
+      }
+      if (lane == 0) s_blk[kSparseMaxBlocks] = cnt < kSparseMaxBlocks ? cnt : kSparseMaxBlocks;
+    }
+    __syncthreads();
+    ns = __builtin_amdgcn_readfirstlane(s_blk[kSparseMaxBlocks]);
+  }
+  // first key of stage i: consecutive 64-key stages, or the listed blocks in list order
+  auto stage_key = [&](int i) {
+    if constexpr (MODE == kModeSparse) return __builtin_amdgcn_readfirstlane(s_blk[i]) * SK;
+    else return i * SK;
+  };
 
   TileState<D, QB> st;
 #pragma unroll
@@ -501,7 +547,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     src_v[i] = logical_src<D, false>(P, vbytes);
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
-    const int kb = stage * SK;
+    const int kb = stage_key(stage);
     const int rows = (Lk - kb < SK) ? (Lk - kb) : SK;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * k_rs), 0, rows * kbytes, kRsrcFlags);
@@ -527,12 +573,12 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
     stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
-                      issue_fn, s, Lk, koff, voff, c, g);
+                      issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
     if (s + 1 >= ns) break;
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
     stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
-                      issue_fn, s + 1, Lk, koff, voff, c, g);
+                      issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
   }
   __syncthreads();   // every wave has left the ring
 
@@ -588,6 +634,7 @@ pfa_fwd_kernel(Params p) {
   __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
   int* s_order = reinterpret_cast<int*>(smem + 2 * kStages * C::TILE_BYTES);
   int* s_prefix = s_order + kSortMax;
+  int* s_blk = s_order + C::SCHED_INTS;     // block-sparse variant only (its LDS is larger)
   int* s_len = reinterpret_cast<int*>(ks);  // scratch, dead before the first K tile lands
 
   const int Tq = p.cu_q[p.num_seqs];
@@ -643,7 +690,7 @@ pfa_fwd_kernel(Params p) {
       if (Lk > Tk - ka) Lk = Tk - ka;
       if (Lk < 0) Lk = 0;
     }
-    process_tile<D, QB, NW, SK, MODE>(p, ks, vs, qa, Lq, ka, Lk, h, qt, Tq);
+    process_tile<D, QB, NW, SK, MODE>(p, ks, vs, s_blk, s, qa, Lq, ka, Lk, h, qt, Tq);
   }
 }
 
@@ -1239,12 +1286,14 @@ struct Variant {
 template <int D, int QB, int NW, int SK, int WPE, int MODE>
 Variant make_variant() {
   using C = Tile<D, QB, NW, SK>;
+  static_assert(MODE != kModeSparse || (C::BM == PFA_SPARSE_BLOCK_Q && SK == PFA_SPARSE_BLOCK_K),
+                "the block-sparse layout's blocks are the kernel's query tile and key stage");
   return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, MODE>), C::BM,
-                 C::THREADS, C::LDS_BYTES};
+                 C::THREADS, C::LDS_BYTES + (MODE == kModeSparse ? kSparseLdsBytes : 0)};
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 6;  // head_dim 64, 128 x the three kernel modes
+constexpr int kVariants = 8;  // head_dim 64, 128 x the four kernel modes
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 std::atomic<int> g_bwd_occ[kMaxDevices][2][2];   // [device][head_dim 64 / 128][dK-dV / dQ]
@@ -1283,9 +1332,10 @@ Variant variant_of(int head_dim) {
 }
 
 Variant variant_for(int head_dim, int mode) {
-  return mode == kModeCross ? variant_of<kModeCross>(head_dim)
-       : mode == kModeQkv   ? variant_of<kModeQkv>(head_dim)
-                            : variant_of<kModeSelf>(head_dim);
+  return mode == kModeCross  ? variant_of<kModeCross>(head_dim)
+       : mode == kModeQkv    ? variant_of<kModeQkv>(head_dim)
+       : mode == kModeSparse ? variant_of<kModeSparse>(head_dim)
+                             : variant_of<kModeSelf>(head_dim);
 }
 
 // compute units of the current device (cached; a race only recomputes the same value)
@@ -1354,6 +1404,7 @@ PFA_API const char* pfa_status_string(int status) {
     case PFA_ERR_LAUNCH: return "kernel launch failed";
     case PFA_ERR_SIZE: return "problem size exceeds the supported index range";
     case PFA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+    case PFA_ERR_LAYOUT: return "block-sparse layout is malformed (layout_heads, nnz, row pointers or block indices)";
     default: return "unknown status";
   }
 }
@@ -1480,6 +1531,86 @@ PFA_API int pfa_varlen_fwd_qkv(const void* qkv, const float* rope_cos, const flo
       return PFA_ERR_LAUNCH;
   }
   return launch_fwd(prm, kModeQkv, max_seqlen, head_dim, stream);
+}
+
+PFA_API int pfa_varlen_fwd_blocksparse(const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                                       int heads, int head_dim, float scale, const int32_t* kv_ptr,
+                                       const int32_t* kv_idx, int nnz, int layout_heads, void* out,
+                                       float* lse, hipStream_t stream) {
+  // ---- argument checks: all before any HIP runtime call
+  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens == nullptr || out == nullptr ||
+      kv_ptr == nullptr || (kv_idx == nullptr && nnz > 0))
+    return PFA_ERR_NULL;
+  if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (max_seqlen < 1) return PFA_ERR_MAX_SEQLEN;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
+  if (nnz < 0 || (layout_heads != 1 && layout_heads != heads)) return PFA_ERR_LAYOUT;
+  const void* ins[6] = {q, k, v, cu_seqlens, kv_ptr, kv_idx};
+  for (const void* in : ins)
+    if (in != nullptr && (in == out || (lse != nullptr && in == static_cast<const void*>(lse))))
+      return PFA_ERR_ALIAS;
+  if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
+  if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
+  if ((int64_t)max_seqlen > (int64_t)kSparseMaxBlocks * PFA_SPARSE_BLOCK_K) return PFA_ERR_SIZE;
+  const int64_t qt_max = ((int64_t)max_seqlen + PFA_SPARSE_BLOCK_Q - 1) / PFA_SPARSE_BLOCK_Q;
+  if ((int64_t)num_seqs * heads * qt_max > INT32_MAX) return PFA_ERR_SIZE;
+
+  Params prm{};
+  prm.q = static_cast<const __bf16*>(q);
+  prm.k = static_cast<const __bf16*>(k);
+  prm.v = static_cast<const __bf16*>(v);
+  prm.cu_q = cu_seqlens;
+  prm.cu_k = cu_seqlens;
+  prm.out = static_cast<__bf16*>(out);
+  prm.lse = lse;
+  prm.num_seqs = num_seqs;
+  prm.heads = heads;
+  prm.c = scale * kLog2e;
+  prm.kv_ptr = kv_ptr;
+  prm.kv_idx = kv_idx;
+  prm.nnz = nnz;
+  prm.layout_heads = layout_heads;
+  return launch_fwd(prm, kModeSparse, max_seqlen, head_dim, stream);
+}
+
+PFA_API int pfa_check_block_layout(const int32_t* cu_host, int num_seqs, int max_seqlen, int heads,
+                                   int layout_heads, const int32_t* kv_ptr_host,
+                                   const int32_t* kv_idx_host, int nnz) {
+  int64_t total = 0;
+  const int rc = pfa_check_cu_seqlens(cu_host, num_seqs, max_seqlen, &total);
+  if (rc != PFA_OK) return rc;
+  if (kv_ptr_host == nullptr || (kv_idx_host == nullptr && nnz > 0)) return PFA_ERR_NULL;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (nnz < 0 || (layout_heads != 1 && layout_heads != heads)) return PFA_ERR_LAYOUT;
+  if ((int64_t)max_seqlen > (int64_t)kSparseMaxBlocks * PFA_SPARSE_BLOCK_K) return PFA_ERR_SIZE;
+  const int64_t qt_max = ((int64_t)max_seqlen + PFA_SPARSE_BLOCK_Q - 1) / PFA_SPARSE_BLOCK_Q;
+  const int64_t rows = (int64_t)num_seqs * layout_heads * qt_max;
+  if (rows > INT32_MAX) return PFA_ERR_SIZE;
+  if (kv_ptr_host[0] != 0 || kv_ptr_host[rows] != nnz) return PFA_ERR_LAYOUT;
+  std::vector<int> seen((size_t)kSparseMaxBlocks, -1);   // row that last listed each block
+  for (int64_t r = 0; r < rows; ++r) {
+    const int64_t e0 = kv_ptr_host[r], e1 = kv_ptr_host[r + 1];
+    if (e1 < e0 || e1 > nnz) return PFA_ERR_LAYOUT;
+    const int64_t qt = r % qt_max;
+    const int s = (int)(r / qt_max / layout_heads);
+    const int64_t L = (int64_t)cu_host[s + 1] - cu_host[s];
+    const int64_t tiles = (L + PFA_SPARSE_BLOCK_Q - 1) / PFA_SPARSE_BLOCK_Q;
+    const int64_t nkb = (L + PFA_SPARSE_BLOCK_K - 1) / PFA_SPARSE_BLOCK_K;
+    if (qt >= tiles) {                 // no such query tile: the row must be empty
+      if (e1 != e0) return PFA_ERR_LAYOUT;
+      continue;
+    }
+    if (e1 == e0) return PFA_ERR_LAYOUT;   // a query block with no keys has no softmax
+    for (int64_t e = e0; e < e1; ++e) {
+      const int b = kv_idx_host[e];
+      if (b < 0 || b >= nkb || seen[(size_t)b] == (int)r) return PFA_ERR_LAYOUT;
+      seen[(size_t)b] = (int)r;
+    }
+  }
+  return PFA_OK;
 }
 
 PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,

@@ -27,6 +27,7 @@ def declared_symbols():
 
 def test_header_declares_the_abi():
     assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv",
+                                       "pfa_varlen_fwd_blocksparse", "pfa_check_block_layout",
                                        "pfa_varlen_bwd", "pfa_attn_merge",
                                        "pfa_check_cu_seqlens", "pfa_status_string"}
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-12, 1):
+    for code in range(-13, 1):
         assert lib.pfa_status_string(code)
     assert lib.pfa_status_string(-999) == b"unknown status"
 
@@ -117,6 +118,72 @@ def test_qkv_argument_checks_run_before_any_hip_call(lib):
     assert _qkv(lib, sin=52) == -12
     assert _qkv(lib, heads=2**16, head_dim=64) == -11      # 3 * H * d over 2^23
     assert _qkv(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
+
+
+def _sparse(lib, q=16, k=32, v=48, cu=64, num_seqs=1, max_seqlen=1, heads=2, head_dim=64,
+            scale=1.0, kv_ptr=80, kv_idx=96, nnz=1, layout_heads=1, out=112, lse=128):
+    return lib.pfa_varlen_fwd_blocksparse(q, k, v, cu, num_seqs, max_seqlen, heads, head_dim, scale,
+                                          kv_ptr, kv_idx, nnz, layout_heads, out, lse, None)
+
+
+def test_blocksparse_argument_checks_run_before_any_hip_call(lib):
+    for name in ("q", "k", "v", "cu", "out", "kv_ptr"):
+        assert _sparse(lib, **{name: None}) == -1, name
+    assert _sparse(lib, kv_idx=None) == -1                  # entries promised but no array
+    assert _sparse(lib, num_seqs=0) == -2
+    assert _sparse(lib, heads=0) == -3
+    assert _sparse(lib, max_seqlen=0) == -4
+    assert _sparse(lib, head_dim=80) == -5
+    assert _sparse(lib, scale=-1.0) == -6
+    assert _sparse(lib, nnz=-1) == -13
+    assert _sparse(lib, layout_heads=3) == -13               # neither 1 nor heads
+    assert _sparse(lib, layout_heads=0) == -13
+    assert _sparse(lib, out=96) == -7                        # out is the index array
+    assert _sparse(lib, lse=80) == -7
+    assert _sparse(lib, lse=112) == -7
+    assert _sparse(lib, max_seqlen=65537) == -11             # beyond the LDS list
+    assert _sparse(lib, heads=2**17, head_dim=128) == -11
+
+
+def test_block_layout_validator():
+    from packed_varlen_flash_amd import PfaError, block_layout_csr, pfa_check_block_layout
+    lengths = [300, 0, 64, 1]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    good = [[[0, 1, 4], [2, 3]], [], [[0]], [[0]]]
+    kv_ptr, kv_idx, lh = block_layout_csr([good], lengths, 300)
+    assert lh == 1 and kv_ptr.shape[0] == 4 * 2 + 1 and kv_idx.tolist() == [0, 1, 4, 2, 3, 0, 0]
+    pfa_check_block_layout(cu, 300, 2, 1, kv_ptr, kv_idx)
+    per_head = [good, [[[4, 0], [1]], [], [[0]], [[0]]]]
+    p2, i2, lh2 = block_layout_csr(per_head, lengths, 300)
+    pfa_check_block_layout(cu, 300, 2, 2, p2, i2)
+    with pytest.raises(PfaError) as e:
+        pfa_check_block_layout(cu, 300, 3, 2, p2, i2)         # layout_heads neither 1 nor heads
+    assert e.value.status == -13
+
+    def bad(layout):
+        p, i, l = block_layout_csr([layout], lengths, 300)
+        with pytest.raises(PfaError) as e:
+            pfa_check_block_layout(cu, 300, 2, l, p, i)
+        assert e.value.status == -13
+
+    bad([[[0, 1, 5], [2]], [], [[0]], [[0]]])      # block 5 is past the 300-token segment
+    bad([[[0, 1, 1], [2]], [], [[0]], [[0]]])      # repeated block
+    bad([[[0], []], [], [[0]], [[0]]])             # a query block with no keys
+    bad([[[0], [1]], [], [[0], [0]], [[0]]])       # a query block the 64-token segment lacks
+    bad([[[0], [-1]], [], [[0]], [[0]]])
+    p, i, _ = block_layout_csr([good], lengths, 300)
+    p_bad = p.copy()
+    p_bad[-1] += 1                                 # does not end at nnz
+    with pytest.raises(PfaError):
+        pfa_check_block_layout(cu, 300, 2, 1, p_bad, i)
+    p_bad = p.copy()
+    p_bad[1], p_bad[2] = p_bad[2], p_bad[1]        # decreasing (0, 5, 3, ...)
+    assert p_bad[1] > p_bad[2]
+    with pytest.raises(PfaError):
+        pfa_check_block_layout(cu, 300, 2, 1, p_bad, i)
+    with pytest.raises(PfaError) as e:
+        pfa_check_block_layout(cu, 200, 2, 1, np.zeros(5, np.int32), i)
+    assert e.value.status == -8                    # cu_seqlens has a segment over max_seqlen
 
 
 def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):

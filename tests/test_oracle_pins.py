@@ -763,8 +763,8 @@ def test_blocksparse_list_order_out_of_range_and_empty_rows():
     np.testing.assert_allclose(l2, l, rtol=0, atol=1e-13)
     rows = np.array([0, 255, 256, 699, 700, 789])
     o3, l3 = oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, lay, rows=rows)
-    np.testing.assert_array_equal(o3, o[rows])
-    np.testing.assert_array_equal(l3, l[:, rows])
+    np.testing.assert_allclose(o3, o[rows], rtol=0, atol=1e-14)   # BLAS may block rows differently
+    np.testing.assert_allclose(l3, l[:, rows], rtol=0, atol=1e-13)
     bad = [[[r + r[:1] for r in seg] for seg in lay[0]]]
     with pytest.raises(ValueError):
         oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, bad)
