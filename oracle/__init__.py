@@ -25,6 +25,10 @@ marshals:
 * ``varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale, layout, block_q, block_k, rows)``:
   restricted attention over listed key blocks per (segment, head, query block), numpy
   fp64; ``block_lists_from_mask`` turns a token mask into such lists.
+* FP8 P.V variant: ``e4m3_round``, ``e4m3_encode``, ``e4m3_decode``, ``v_scale_exponent``,
+  ``quantize_v_fp8`` (per (segment, head, channel) power-of-two scales, e4m3 codes),
+  ``varlen_fwd_fp8pv_blocked`` (the blocked steps with FP8 weights and V, fp64) and
+  ``fp8pv_error_bound`` (per-element bound against exact attention on the dequantised V).
 * ``widen_bf16(bits)`` / ``round_bf16_bits(x)``: bf16 bits to fp64 and back (one
   rounding, ties to even).
 * ``probs(q, k, cu_seqlens, scale, i, h)`` -> one row of the block-diagonal
@@ -37,6 +41,7 @@ sequence packing).
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -312,6 +317,156 @@ def varlen_fwd_blocksparse(q, k, v, cu_seqlens, scale: float, layout, block_q: i
                 out[dst, h] = (w @ v[kk, h]) / z
                 lse[h, dst] = (m + np.log(z))[:, 0]
     return out, lse
+
+
+# ------------------------------------------------------------------ FP8 P.V variant
+# The FPS Attention slides (tool.lu deck on accelerating multimodal generation, slides
+# 35-38) combine sliding-tile sparsity with FP8 attention: V quantised per channel, the
+# probabilities P per tensor, and a dequantising FlashAttention.  Readings taken here (the
+# slides give no formulas): FP8 is OCP e4m3 (3 mantissa bits, bias 7, largest finite 448,
+# subnormal step 2^-9); V's scale is a power of two per (segment, head, channel), the
+# smallest with max|V| / scale <= 448; P is scaled by the fixed per-tensor factor 2^8 (its
+# range is (0, 1] under the online softmax) before rounding to e4m3.
+
+E4M3_MAX = 448.0
+P_SCALE_LOG2 = 8
+
+
+def e4m3_round(x):
+    """Round fp64 values (|x| <= 448) to the nearest e4m3 value, ties to even: 3 fraction
+    bits for |x| >= 2^-6, a fixed step of 2^-9 below.  Returns the rounded fp64 values."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.abs(x) > E4M3_MAX):
+        raise ValueError("e4m3_round: |x| > 448")
+    m, e = np.frexp(x)                       # x = m 2^e, 0.5 <= |m| < 1
+    normal = np.abs(x) >= 2.0 ** -6
+    r_norm = np.ldexp(np.rint(m * 16.0), e - 4)         # 4 significant bits
+    r_sub = np.rint(x * 2.0 ** 9) * 2.0 ** -9
+    return np.where(normal, r_norm, r_sub)
+
+
+def e4m3_encode(x):
+    """e4m3 codes (uint8) of values that are already e4m3 numbers (see e4m3_round)."""
+    x = np.asarray(x, dtype=np.float64)
+    sign = (np.signbit(x)).astype(np.uint8) << 7
+    a = np.abs(x)
+    m, e = np.frexp(np.where(a > 0, a, 1.0))            # a = m 2^e
+    normal = a >= 2.0 ** -6
+    exp_field = np.where(normal, e - 1 + 7, 0)            # a = 1.f * 2^(e-1)
+    frac = np.where(normal, np.rint((m * 2.0 - 1.0) * 8.0), np.rint(a * 2.0 ** 9))
+    code = np.where(normal, (exp_field.astype(np.int64) << 3) | frac.astype(np.int64),
+                    frac.astype(np.int64))
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(codes):
+    """Values of e4m3 codes (0x7F / 0xFF, the NaN codes, are not expected)."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ef, f = (c >> 3) & 0xF, c & 0x7
+    val = np.where(ef == 0, f * 2.0 ** -9, np.ldexp(1.0 + f / 8.0, ef - 7))
+    return sign * val
+
+
+def v_scale_exponent(amax):
+    """Smallest integer e with amax * 2^-e <= 448 (0 when amax is 0)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    m, E = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = m 2^E, 0.5 <= m < 1
+    e = np.where(m <= 0.875, E - 9, E - 8)               # 448 = 0.875 * 2^9
+    return np.where(amax > 0, e, 0).astype(np.int64)
+
+
+def quantize_v_fp8(v_bits, cu_seqlens):
+    """Per (segment, head, channel) power-of-two scaling of V and e4m3 rounding.
+    Returns (codes uint8 [T, H, d], scales fp64 [S, H, d], each an exact power of two);
+    V[t, h, c] is approximated by decode(codes[t, h, c]) * scales[s(t), h, c]."""
+    v = widen_bf16(v_bits) if np.asarray(v_bits).dtype == np.uint16 else np.asarray(v_bits, np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, d = v.shape
+    S = cu.shape[0] - 1
+    codes = np.zeros((T, H, d), dtype=np.uint8)
+    scales = np.ones((S, H, d))
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b <= a:
+            continue
+        e = v_scale_exponent(np.abs(v[a:b]).max(axis=0))      # [H, d]
+        scales[s] = np.ldexp(1.0, e)
+        codes[a:b] = e4m3_encode(e4m3_round(v[a:b] / scales[s][None]))
+    return codes, scales
+
+
+def dequantize_v_fp8(codes, scales, cu_seqlens):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    seg = np.searchsorted(cu[1:], np.arange(codes.shape[0]), side="right")
+    return e4m3_decode(codes) * scales[seg]
+
+
+def varlen_fwd_fp8pv_blocked(q, k, v_codes, v_scales, cu_seqlens, scale: float, block: int = 64,
+                             quantize: bool = True, rows=None):
+    """The blocked online softmax (GigaPath-Flash page, section 3.2) with the P.V product in
+    FP8, in fp64: per query row and 64-key block in order, the running maximum m (base 2)
+    is raised to the block's maximum, accumulator and row sum are rescaled, the weights
+    w = 2^8 2^(s log2(e) - m) are summed unrounded into l and rounded to e4m3 for the
+    product with the e4m3 values of V; finally O = acc * scale_V / l and
+    LSE = ln 2 (m - 8 + log2 l).  quantize=False keeps w unrounded (then the result is
+    plain attention on the dequantised V)."""
+    q = widen_bf16(q) if np.asarray(q).dtype == np.uint16 else np.asarray(q, np.float64)
+    k = widen_bf16(k) if np.asarray(k).dtype == np.uint16 else np.asarray(k, np.float64)
+    v8 = e4m3_decode(v_codes)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, d = q.shape
+    want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    seg_of = np.searchsorted(cu[1:], want, side="right")
+    out = np.zeros((want.shape[0], H, d))
+    lse = np.full((H, want.shape[0]), -np.inf)
+    c = scale / math.log(2.0)
+    for s in np.unique(seg_of):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        sel = np.nonzero(seg_of == s)[0]
+        qi = want[sel]
+        for h in range(H):
+            m = np.full(sel.shape[0], -np.inf)
+            l = np.zeros(sel.shape[0])
+            acc = np.zeros((sel.shape[0], d))
+            for b0 in range(0, L, block):
+                kk = np.arange(a + b0, a + min(b0 + block, L))
+                sc = (q[qi, h] @ k[kk, h].T) * c
+                m_new = np.maximum(m, sc.max(axis=1))
+                alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m_new))
+                w = np.exp2(sc - m_new[:, None] + P_SCALE_LOG2)
+                l = l * alpha + w.sum(axis=1)
+                wq = e4m3_round(w) if quantize else w
+                acc = acc * alpha[:, None] + wq @ v8[kk, h]
+                m = m_new
+            out[sel, h] = acc * v_scales[s, h][None, :] / l[:, None]
+            lse[h, sel] = math.log(2.0) * (m - P_SCALE_LOG2 + np.log2(l))
+    return out, lse
+
+
+def fp8pv_error_bound(q, k, v_codes, v_scales, cu_seqlens, scale: float, rows=None):
+    """Per-element bound on |O_fp8 - O| for O the exact attention on the dequantised V:
+    O_fp8 = sum_j w8_j V_j / sum_j w_j with the same unrounded normaliser, and each e4m3
+    weight is within max(2^-4 w_j, 2^-10) of w_j (half a step: relative 2^-4 for normal
+    values, 2^-10 absolute below 2^-6).  With w_j = 2^8 p_j 2^(m_stage - M) <= 2^8 p_j,
+    the error is at most sum_j (2^-4 p_j + 2^-18) |V_j| / sum_j p_j.  fp64, [n, H, d]."""
+    q = widen_bf16(q) if np.asarray(q).dtype == np.uint16 else np.asarray(q, np.float64)
+    k = widen_bf16(k) if np.asarray(k).dtype == np.uint16 else np.asarray(k, np.float64)
+    vd = np.abs(dequantize_v_fp8(v_codes, v_scales, cu_seqlens))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, d = q.shape
+    want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    seg_of = np.searchsorted(cu[1:], want, side="right")
+    bound = np.zeros((want.shape[0], H, d))
+    for s in np.unique(seg_of):
+        a, b = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero(seg_of == s)[0]
+        for h in range(H):
+            sc = scale * (q[want[sel], h] @ k[a:b, h].T)
+            p = np.exp(sc - sc.max(axis=1, keepdims=True))
+            bound[sel, h] = (2.0 ** -4 * (p @ vd[a:b, h]) + 2.0 ** -18 * vd[a:b, h].sum(axis=0)) \
+                / p.sum(axis=1, keepdims=True)
+    return bound
 
 
 def merge(o_a, lse_a, o_b, lse_b):

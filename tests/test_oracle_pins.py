@@ -768,3 +768,94 @@ def test_blocksparse_list_order_out_of_range_and_empty_rows():
     bad = [[[r + r[:1] for r in seg] for seg in lay[0]]]
     with pytest.raises(ValueError):
         oracle.varlen_fwd_blocksparse(w.q, w.k, w.v, w.cu_seqlens, w.scale, bad)
+
+
+# ---------------------------------------------------------------- FP8 P.V variant
+# FPS Attention slides (tool.lu deck on accelerating multimodal generation, slides 35-38):
+# V per channel, P per tensor, FP8 attention with dequantisation.  Readings: OCP e4m3,
+# power-of-two V scales per (segment, head, channel), P scaled by 2^8.
+
+def test_e4m3_rounding_matches_torch_float8():
+    """torch's float8_e4m3fn conversion (round to nearest even) is an independent routine."""
+    rng = np.random.default_rng(50)
+    x = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-2.0 ** -5, 2.0 ** -5, 4000),
+                        np.ldexp(rng.integers(-600, 600, 2000) + 0.5, -10),   # exact ties
+                        np.ldexp(rng.integers(1, 64, 500) * 2 + 1, rng.integers(-4, 3, 500)),
+                        [0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10]])
+    x = x[np.abs(x) <= 448]
+    x = x.astype(np.float32).astype(np.float64)          # torch converts from float32
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(oracle.e4m3_encode(oracle.e4m3_round(x)), ref.view(torch.uint8).numpy())
+    np.testing.assert_array_equal(oracle.e4m3_round(x), ref.to(torch.float64).numpy())
+
+
+def test_e4m3_codes_round_trip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    assert vals.max() == 448.0 and vals[codes == 0x01][0] == 2.0 ** -9
+    back = oracle.e4m3_encode(vals)
+    same = (back == codes) | ((codes == 0x80) & (back == 0x80))
+    assert np.all(same)
+    np.testing.assert_array_equal(oracle.e4m3_round(vals), vals)
+
+
+def test_v_scale_exponent_is_the_smallest_that_fits():
+    rng = np.random.default_rng(51)
+    amax = np.concatenate([np.exp(rng.uniform(-20, 20, 5000)), [448.0, 449.0, 224.0, 1.0, 0.875 * 2 ** 9]])
+    e = oracle.v_scale_exponent(amax)
+    assert np.all(amax * 2.0 ** -e <= 448.0) and np.all(amax * 2.0 ** -(e - 1) > 448.0)
+    assert list(oracle.v_scale_exponent(np.array([448.0, 449.0, 0.0]))) == [0, 1, 0]
+
+
+def test_quantize_v_per_segment_channel():
+    w = W.make([40, 0, 33, 1], 3, 16, seed=52)
+    v = W.bf16_to_f64(w.v)
+    v[0:40, 1, 5] = 0.0                                   # an all-zero channel of segment 0
+    vb = W.bf16_bits(v.astype(np.float32))
+    codes, scales = oracle.quantize_v_fp8(vb, w.cu_seqlens)
+    assert scales[0, 1, 5] == 1.0 and np.all(codes[0:40, 1, 5] == 0)
+    deq = oracle.dequantize_v_fp8(codes, scales, w.cu_seqlens)
+    vv = W.bf16_to_f64(vb)
+    seg = np.searchsorted(w.cu_seqlens[1:], np.arange(w.total_tokens), side="right")
+    step = np.maximum(np.abs(vv) * 2.0 ** -4, 2.0 ** -10 * scales[seg])
+    assert np.all(np.abs(deq - vv) <= step + 1e-300)
+    for s, (a, b) in enumerate(zip(w.cu_seqlens[:-1], w.cu_seqlens[1:])):   # segments alone
+        if b > a:
+            c1, s1 = oracle.quantize_v_fp8(vb[a:b], [0, b - a])
+            np.testing.assert_array_equal(c1, codes[a:b])
+            np.testing.assert_array_equal(s1[0], scales[s])
+    m = np.abs(vv[40:73]).max(axis=0) / scales[2]          # the scale uses the fp8 range
+    assert np.all((m > 224) & (m <= 448))
+
+
+def test_fp8pv_blocked_steps_without_rounding_are_exact_attention():
+    w = W.make([130, 1, 64, 200], 2, 32, seed=53)
+    codes, scales = oracle.quantize_v_fp8(w.v, w.cu_seqlens)
+    o, l = oracle.varlen_fwd_fp8pv_blocked(w.q, w.k, codes, scales, w.cu_seqlens, w.scale, quantize=False)
+    vd = oracle.dequantize_v_fp8(codes, scales, w.cu_seqlens)
+    o_ref, l_ref = oracle.varlen_fwd(W.bf16_to_f64(w.q), W.bf16_to_f64(w.k), vd, w.cu_seqlens, w.scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("qk_scale", [1.0, 4.0])
+def test_fp8pv_blocked_steps_stay_within_the_bound(qk_scale):
+    """The FP8 steps differ from exact attention on the dequantised V by at most the
+    rounding of each weight (relative 2^-4, absolute 2^-10 in the 2^8-scaled units); the
+    bound is reached to within a small factor, so it is not vacuous."""
+    w = W.make([300, 77, 520], 2, 64, seed=54)
+    q = W.bf16_bits((W.bf16_to_f64(w.q) * qk_scale).astype(np.float32))
+    codes, scales = oracle.quantize_v_fp8(w.v, w.cu_seqlens)
+    o, l = oracle.varlen_fwd_fp8pv_blocked(q, w.k, codes, scales, w.cu_seqlens, w.scale)
+    vd = oracle.dequantize_v_fp8(codes, scales, w.cu_seqlens)
+    o_ref, l_ref = oracle.varlen_fwd(W.bf16_to_f64(q), W.bf16_to_f64(w.k), vd, w.cu_seqlens, w.scale)
+    bound = oracle.fp8pv_error_bound(q, w.k, codes, scales, w.cu_seqlens, w.scale)
+    err = np.abs(o - o_ref)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-13)
+    assert (err / bound).max() > 0.1
+    np.testing.assert_allclose(l, l_ref, rtol=0, atol=1e-12)     # LSE uses unrounded weights
+    rows = np.array([0, 299, 300, 376, 377, 896])
+    o2, l2 = oracle.varlen_fwd_fp8pv_blocked(q, w.k, codes, scales, w.cu_seqlens, w.scale, rows=rows)
+    np.testing.assert_allclose(o2, o[rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.fp8pv_error_bound(q, w.k, codes, scales, w.cu_seqlens, w.scale,
+                                                        rows=rows), bound[rows], rtol=1e-12, atol=0)
