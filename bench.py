@@ -17,6 +17,7 @@ row sample of the same workload.
     python bench.py --op bwd             # backward (dQ, dK, dV) on the same pack
     python bench.py --op qkv             # fused [T,3,H,d] input with 2-D RoPE, same pack
     python bench.py --op sparse          # block-sparse band layout (+-1024 tokens), same pack
+    python bench.py --op fp8pv           # P.V in FP8 (V quantised per segment/head/channel)
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -483,13 +484,112 @@ def bench_sparse(args):
     print(json.dumps(rec), flush=True)
 
 
+PEAK_FP8_TFLOPS = 5000.0             # MI355X dense fp8 MFMA (published)
+
+
+def bench_fp8pv(args):
+    """The forward with P.V in FP8: V quantised once (per segment, head and channel), then
+    q.k in bf16 and P.V on the FP8 matrix cores.  The quantiser is timed on its own; the
+    attention kernel's roofline takes half the counted work at the bf16 rate and half at
+    the fp8 rate (2 / (1/2.5 + 1/5) = 3.33 PFLOP/s)."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import pfa_quantize_v_fp8, pfa_varlen_fwd, pfa_varlen_fwd_fp8pv
+    wl = W.generate(args.config, seed=args.seed)
+    T, H, d = wl.total_tokens, wl.heads, wl.head_dim
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    v8 = torch.empty((T, H, d), dtype=torch.uint8, device=dev)
+    vs = torch.empty((wl.num_seqs, H, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def quant():
+        pfa_quantize_v_fp8(v, cu, v8=v8, v_scale=vs, stream=stream)
+
+    def step():
+        pfa_varlen_fwd_fp8pv(q, k, v8, vs, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
+
+    def step_bf16():
+        pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
+
+    ms_bf16, _ = timed(step_bf16, stream, args.steps, args.warmup)
+    ms_q, _ = timed(quant, stream, args.steps, args.warmup)
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    peak = 2.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(1234)
+        t0 = time.perf_counter()
+        codes, scales = oracle.quantize_v_fp8(wl.v, wl.cu_seqlens)
+        t_quant = time.perf_counter() - t0
+        pilot = np.sort(rng.choice(T, size=24, replace=False))
+        t0 = time.perf_counter()
+        oracle.varlen_fwd_fp8pv_blocked(wl.q, wl.k, codes, scales, wl.cu_seqlens, wl.scale, rows=pilot)
+        per_row = (time.perf_counter() - t0) / len(pilot)
+        n = int(max(24, min(T, args.cpu_budget / max(per_row, 1e-9))))
+        for attempt in range(2):
+            rows = np.sort(rng.choice(T, size=n, replace=False))
+            t0 = time.perf_counter()
+            o_em, l_em = oracle.varlen_fwd_fp8pv_blocked(wl.q, wl.k, codes, scales, wl.cu_seqlens,
+                                                         wl.scale, rows=rows)
+            dt = time.perf_counter() - t0
+            if attempt == 1 or n == T or dt > args.cpu_budget / 2:
+                break
+            n = int(min(T, n * args.cpu_budget / max(dt, 1e-3)))
+        seg = np.searchsorted(wl.cu_seqlens[1:], rows, side="right")
+        flop = 4.0 * float(np.diff(wl.cu_seqlens)[seg].astype(np.float64).sum()) * H * d
+        o = W.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        vd = oracle.dequantize_v_fp8(codes, scales, wl.cu_seqlens)
+        o_ex, _ = oracle.varlen_fwd(W.bf16_to_f64(wl.q), W.bf16_to_f64(wl.k), vd, wl.cu_seqlens,
+                                    wl.scale, rows=rows)
+        bound = oracle.fp8pv_error_bound(wl.q, wl.k, codes, scales, wl.cu_seqlens, wl.scale, rows=rows)
+        err = np.abs(o - o_ex)
+        rr = lambda a, b: float(np.sqrt(((a - b) ** 2).sum() / (b ** 2).sum()))
+        parity = {"rows": int(n),
+                  "codes_equal_oracle": bool(np.array_equal(v8.cpu().numpy(), codes)),
+                  "max_abs_err_vs_exact_on_dequantised_v": float(err.max()),
+                  "max_err_over_fp8_bound": float((err / (bound + 1e-30)).max()),
+                  "rel_rms_vs_exact": rr(o, o_ex), "rel_rms_vs_fp8_steps": rr(o, o_em),
+                  "lse_max_abs_err": float(np.abs(lse.cpu().numpy()[:, rows] - l_em).max())}
+        from threadpoolctl import threadpool_info
+        blas = [x["num_threads"] for x in threadpool_info() if x.get("user_api") == "blas"]
+        cpu = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": max(blas) if blas else 1,
+               "kind": "oracle",
+               "sample": f"{n} uniformly drawn query rows of {wl.name} through the blocked FP8 steps "
+                         f"(numpy fp64): {flop / 1e9:.1f} GFLOP in {dt:.1f} s; the V quantiser on "
+                         f"the whole V took {t_quant:.1f} s"}
+    achieved = wl.flops / (kms * 1e-3) / 1e12
+    vbytes = T * H * d
+    rec = {"metric": "FP8 P.V attention TFLOP/s (4·ΣL_i²·H·d), 1 GPU",
+           "value": round(wl.flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 QK, e4m3 PV",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V; V quantised by the library)",
+           "config": {"workload": describe(wl) + "; V in e4m3 per (segment, head, channel)",
+                      "segments": list(wl.lengths), "heads": H, "head_dim": d,
+                      "flop_per_step": wl.flops, "seed": args.seed},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5)},
+           "bf16_forward_ms": round(ms_bf16, 5), "speedup_vs_bf16": round(ms_bf16 / ms, 3),
+           "quantize_ms": round(ms_q, 5),
+           "quantize_gbs": round((vbytes * 2 * 2 + vbytes) / (ms_q * 1e-3) / 1e9, 1),
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
-    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv", "sparse"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv", "sparse", "fp8pv"])
     ap.add_argument("--band", type=int, default=1024, help="band radius (tokens) for --op sparse")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -515,6 +615,9 @@ def main():
         return
     if args.op == "sparse":
         bench_sparse(args)
+        return
+    if args.op == "fp8pv":
+        bench_fp8pv(args)
         return
     if args.op == "bwd":
         bench_bwd(args)

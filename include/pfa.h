@@ -216,6 +216,52 @@ PFA_API int pfa_check_block_layout(const int32_t* cu_host, int num_seqs, int max
                                    const int32_t* kv_idx_host, int nnz);
 
 /*
+ * pfa_quantize_v_fp8 -- V in e4m3 for pfa_varlen_fwd_fp8pv.
+ *
+ * The FPS Attention slides (tool.lu deck "[极致]加速多模态生成的算法设计与系统挑战",
+ * slides 35-38) quantise V per channel for an FP8 attention that dequantises as it goes. The
+ * slides fix no format or scale rule. Here every (segment, head, channel) gets a
+ * power-of-two scale 2^e: e is the smallest integer with max_t |V[t,h,c]| * 2^-e <= 448
+ * (the largest OCP e4m3 value), not below -126, and e = 0 for an all-zero channel. The code
+ * of V[t,h,c] is V * 2^-e rounded to e4m3, to nearest even. Scaling by a power of two is
+ * exact, and a segment's scales depend on its own tokens only, so packing does not couple
+ * images.
+ *
+ * v         device bf16 [T, heads, head_dim], 16-byte aligned, finite.
+ * v8        device uint8 [T, heads, head_dim] e4m3 codes, 8-byte aligned (written).
+ * v_scale   device fp32 [num_seqs, heads, head_dim] (written): the scales 2^e. During the
+ *           call it holds the per-channel maxima.
+ * Four kernel launches on stream (HBM-bound). Errors as for pfa_varlen_fwd, plus
+ * PFA_ERR_ALIAS, PFA_ERR_ALIGN, and PFA_ERR_SIZE when num_seqs * heads * head_dim exceeds
+ * 2^31 - 1.
+ */
+PFA_API int pfa_quantize_v_fp8(const void* v, const int32_t* cu_seqlens, int num_seqs, int heads,
+                               int head_dim, void* v8, float* v_scale, hipStream_t stream);
+
+/*
+ * pfa_varlen_fwd_fp8pv -- the packed self-attention forward with P.V in FP8.
+ *
+ * The same blocked online softmax as pfa_varlen_fwd, with q.k in bf16. For every 64-key
+ * block, the weights w = 2^8 * exp(s - m) (m the running row maximum, so w <= 2^8: P
+ * quantised per tensor with the fixed scale 2^8) are rounded to e4m3. They multiply the
+ * e4m3 codes of V on the FP8 matrix cores, with fp32 accumulation. The row sum l adds
+ * the unrounded weights and normalises the output:
+ *     O[i,h,c] = v_scale[s,h,c] * sum_j e4m3(w_ij) v8[j,h,c] / l_i,
+ *     LSE[h,i] = m_i - 8 ln 2 + ln l_i  (as in pfa_varlen_fwd, from unrounded weights).
+ * Each weight's rounding is at most 2^-4 of it (2^-10 absolute below 2^-6). Against exact
+ * attention on the dequantised V, O therefore errs by at most
+ * sum_j (2^-4 p_ij + 2^-18) |V_j| / sum_j p_ij, plus the bf16 rounding of O.
+ *
+ * q, k      bf16 [T, heads, head_dim] as for pfa_varlen_fwd.
+ * v8, v_scale  as written by pfa_quantize_v_fp8 (both 16-byte aligned).
+ * Everything else, ownership and errors as for pfa_varlen_fwd, plus PFA_ERR_ALIGN.
+ */
+PFA_API int pfa_varlen_fwd_fp8pv(const void* q, const void* k, const void* v8, const float* v_scale,
+                                 const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
+                                 int head_dim, float scale, void* out, float* lse,
+                                 hipStream_t stream);
+
+/*
  * pfa_attn_merge -- combine two results for the same queries over disjoint key sets.
  *
  * If (o_a, lse_a) is attention over key set A and (o_b, lse_b) over key set B, the

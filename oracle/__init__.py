@@ -369,10 +369,11 @@ def e4m3_decode(codes):
 
 
 def v_scale_exponent(amax):
-    """Smallest integer e with amax * 2^-e <= 448 (0 when amax is 0)."""
+    """Smallest integer e with amax * 2^-e <= 448 (0 when amax is 0), raised to -126 when
+    smaller so that the scale 2^e stays a normal fp32 number."""
     amax = np.asarray(amax, dtype=np.float64)
     m, E = np.frexp(np.where(amax > 0, amax, 1.0))      # amax = m 2^E, 0.5 <= m < 1
-    e = np.where(m <= 0.875, E - 9, E - 8)               # 448 = 0.875 * 2^9
+    e = np.maximum(np.where(m <= 0.875, E - 9, E - 8), -126)   # 448 = 0.875 * 2^9
     return np.where(amax > 0, e, 0).astype(np.int64)
 
 

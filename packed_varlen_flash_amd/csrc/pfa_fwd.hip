@@ -45,6 +45,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kWave = 64;
 constexpr int kHalf = 64;        // keys per softmax step (two 32-key sub-blocks)
@@ -85,6 +89,10 @@ struct Params {
   const int32_t* kv_idx;
   int nnz;
   int layout_heads;
+  // FP8 P.V variant only: V as e4m3 codes [T, heads, D] and its dequantisation scales
+  // [num_seqs, heads, D] (powers of two)
+  const uint8_t* v8;
+  const float* v_scale;
 };
 
 // Kernel variants: one segment table for queries and keys; separate query and key tables;
@@ -94,6 +102,10 @@ constexpr int kModeSelf = 0;
 constexpr int kModeCross = 1;
 constexpr int kModeQkv = 2;
 constexpr int kModeSparse = 3;   // one table; each query tile reads only its listed key blocks
+constexpr int kModeFp8 = 4;      // one table; P.V in FP8 (e4m3 weights and V)
+// FP8 weights: w = 2^8 p with p = 2^(s log2 e - m) in (0, 1], so w <= 256 < 448 (the
+// largest e4m3 value) and the factor is folded into the exponent.
+constexpr float kP8Log2 = 8.0f;
 // Block-sparse variant: a compacted copy of the tile's key-block list lives in LDS after
 // the schedule (count in the last slot), so segments are limited to this many key blocks.
 constexpr int kSparseMaxBlocks = 1024;
@@ -114,6 +126,8 @@ struct Tile {
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
+  static constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 V row
+  static constexpr int CPT8 = SK * CPR8 / THREADS;  // e4m3 V chunks per thread per stage
   static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
   static_assert(CPT * THREADS == SK * CPR, "stage must split evenly");
   static_assert(SK % kHalf == 0, "stages hold whole 64-key halves");
@@ -134,6 +148,25 @@ __device__ __forceinline__ int phys_off(int row, int chunk) {
   const int line = P >> 4;
   const int sw = IS_K ? swz_k(line) : swz_v(line);
   return ((line << 4) | ((P & 15) ^ sw)) << 4;
+}
+
+// LDS layout of an e4m3 V stage: rows of D bytes (one key each), 16-byte chunks XORed
+// with swz8(row) < D/16.  The transposed byte reads that build the P.V operand have 16
+// lanes read 8 keys x 16 channels: keys 16q + {4g .. 4g+3, 8+4g .. 8+4g+3}, whose bits 1
+// and 3 (d = 128) or bit 3 (d = 64) differ, so the swizzle spreads those 8 rows over
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  return D == 128 ? (((row >> 1) & 1) | (((row >> 3) & 1) << 1)) : ((row >> 3) & 1);
+}
+
+// logical source offset (row * row_bytes + chunk * 16) of the e4m3 V chunk stored at
+// physical chunk position P
+template <int D>
+__device__ __forceinline__ int logical_src8(int P, int row_bytes) {
+  const int row = P / (D / 16);
+  const int pc = P % (D / 16);
+  return row * row_bytes + ((pc ^ swz8<D>(row)) << 4);
 }
 
 // logical byte offset (row * row_bytes + chunk * 16) of the chunk stored at physical
@@ -358,6 +391,80 @@ __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 
   }
 }
 
+// FP8 variant of softmax_body: weights w = 2^(s c - m + 8) rounded to e4m3 (nearest even)
+// four to a register, sub-block `half` filling bytes 16 half .. 16 half + 15 of the P^T
+// operand in the order of the accumulator elements; l_run adds the unrounded weights,
+// which also normalise O.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_body8(TileState<D, QB>& st, const f32x16 (&s)[QB],
+                                              i32x8 (&pw)[QB], int half, float c) {
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float off = kP8Log2 - st.m_run[b];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[b][i], c, off));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 1], c, off));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 2], c, off));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 3], c, off));
+      st.l_run[b] += e0;
+      st.l_run[b] += e1;
+      st.l_run[b] += e2;
+      st.l_run[b] += e3;
+      int w = 0;
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+      pw[b][half * 4 + (i >> 2)] = w;
+    }
+  }
+}
+
+// The V^T operand of one 32-channel output tile for all 64 keys of a stage (e4m3): byte
+// 8q + r of lane (channel, g) is key 16q + 8(r/4) + 4g + r%4, matching the weight bytes
+// of softmax_body8.  Four transposed 8-byte reads; voff8 is the lane's offset for q = 0.
+template <int D>
+__device__ __forceinline__ i32x8 v8_operand(const char* vst, int voff8) {
+  i32x8 a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vst + voff8 + q * 16 * D));
+    a[2 * q] = x[0];
+    a[2 * q + 1] = x[1];
+  }
+  return a;
+}
+
+// One 64-key stage of the FP8 variant: QK and the softmax head as in stage_body, then the
+// weights of both sub-blocks (e4m3) and one 32x32x64 FP8 MFMA per output tile.
+template <int D, int QB, int SK, typename IssueFn>
+__device__ __forceinline__ void stage_body_fp8(TileState<D, QB>& st, char* __restrict__ knext,
+                                               char* __restrict__ vnext, const char* __restrict__ kcur,
+                                               const char* __restrict__ vcur, bool issue,
+                                               const IssueFn& issue_fn, int s, int kbase, int L,
+                                               const int (&koff)[D / 16], const int (&voff8)[D / 32],
+                                               float c, int g) {
+  static_assert(SK == kHalf, "one 64-key head per stage");
+  if (issue) issue_fn(knext, vnext, s + 1);
+  f32x16 s0[QB], s1[QB];
+  i32x8 pw[QB];
+  bf16x8 ka[D / 16], kb[D / 16];
+  k_operands<D>(kcur, koff, ka);
+  k_operands<D>(kcur + 32 * D * 2, koff, kb);
+  qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
+  softmax_head64<D, QB>(st, s0, s1, kbase, L, c, g);
+  softmax_body8<D, QB>(st, s0, pw, 0, c);
+  i32x8 va[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) va[dt] = v8_operand<D>(vcur, voff8[dt]);
+  softmax_body8<D, QB>(st, s1, pw, 1, c);
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      st.o[b][dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[dt], pw[b], st.o[b][dt], 0, 0, 0, 0,
+                                                                   0, 0);
+}
+
 // Interleave n MFMAs with the VALU work around them, `valu` VALU instructions after each.
 template <int N, int VALU>
 __device__ __forceinline__ void interleave_mfma_valu() {
@@ -455,6 +562,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const __bf16* qbase = p.q + (int64_t)qa * q_rs + head_off;
   const __bf16* kbase = p.k + (int64_t)ka * k_rs + head_off;
   const __bf16* vbase = p.v + (int64_t)ka * v_rs + head_off;
+  const uint8_t* v8base = MODE == kModeFp8 ? p.v8 + (int64_t)ka * rs + head_off : nullptr;
   const int q0 = qt * C::BM + wave * (QB * 32);
   int ns = (Lk + SK - 1) / SK;             // LDS stages (0 when the key segment is empty)
   const float c = p.c;
@@ -526,9 +634,19 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   int koff[C::KSTEP], voff[C::DT];
 #pragma unroll
   for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
+  if constexpr (MODE == kModeFp8) {
+    // transposed e4m3 reads: lane i16 supplies row i16/2 (keys 4g + 0..3, then 8 + 4g +
+    // 0..3) and half i16 & 1 of the 16 channels 32dt + 16hh ..; v8_operand adds 16q rows
+    const int r = i16 >> 1;
+    const int row = r < 4 ? 4 * g + r : 8 + 4 * g + (r - 4);
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
-    voff[dt] = phys_off<D, false>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+    for (int dt = 0; dt < C::DT; ++dt)
+      voff[dt] = row * D + (((2 * dt + hh) ^ swz8<D>(row)) << 4) + 8 * (i16 & 1);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      voff[dt] = phys_off<D, false>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+  }
 
   // ---- stage loads: global -> LDS directly (no registers).  Lane l of the wave's i-th
   // load writes physical chunk (wave*CPT + i)*64 + l, fetched from its logical source.
@@ -544,21 +662,35 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   for (int i = 0; i < C::CPT; ++i) {
     const int P = (wave * C::CPT + i) * 64 + lane;
     src_k[i] = logical_src<D, true>(P, kbytes);
-    src_v[i] = logical_src<D, false>(P, vbytes);
+    if constexpr (MODE == kModeFp8) {
+      if (i < C::CPT8) src_v[i] = logical_src8<D>((wave * C::CPT8 + i) * 64 + lane, (int)rs);
+    } else {
+      src_v[i] = logical_src<D, false>(P, vbytes);
+    }
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
     const int kb = stage_key(stage);
     const int rows = (Lk - kb < SK) ? (Lk - kb) : SK;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * k_rs), 0, rows * kbytes, kRsrcFlags);
-    __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * v_rs), 0, rows * vbytes, kRsrcFlags);
     kdst += wave * C::CPT * 1024;
-    vdst += wave * C::CPT * 1024;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
+    for (int i = 0; i < C::CPT; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16, src_k[i], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
+    if constexpr (MODE == kModeFp8) {
+      __amdgpu_buffer_rsrc_t r8 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(v8base + (int64_t)kb * rs), 0, rows * (int)rs, kRsrcFlags);
+      vdst += wave * C::CPT8 * 1024;
+#pragma unroll
+      for (int i = 0; i < C::CPT8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
+    } else {
+      __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * v_rs), 0, rows * vbytes, kRsrcFlags);
+      vdst += wave * C::CPT * 1024;
+#pragma unroll
+      for (int i = 0; i < C::CPT; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
     }
   };
 
@@ -572,13 +704,21 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   for (int s = 0; s < ns; s += 2) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
-                      issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
+    if constexpr (MODE == kModeFp8)
+      stage_body_fp8<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+                                issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
+    else
+      stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+                            issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
     if (s + 1 >= ns) break;
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
-                      issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
+    if constexpr (MODE == kModeFp8)
+      stage_body_fp8<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+                                issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
+    else
+      stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+                            issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
   }
   __syncthreads();   // every wave has left the ring
 
@@ -592,20 +732,28 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = partner_sum(st.l_run[b]);
-    const float lr = partner_sum(st.l_rnd[b]);
+    // FP8: O is normalised by the unrounded weights (l_run), the bf16 paths by the sum of
+    // the rounded ones (l_rnd)
+    const float lr = MODE == kModeFp8 ? lt : partner_sum(st.l_rnd[b]);
     const float inv = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
     const int r = b * 32 + n32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
+        // this lane's channels 32dt + 8ii + 4g + e; FP8 dequantises V per channel here
+        f32x4 sc = {inv, inv, inv, inv};
+        if constexpr (MODE == kModeFp8)
+          sc = inv * *reinterpret_cast<const f32x4*>(p.v_scale + ((int64_t)seg * p.heads + h) * D + 32 * dt +
+                                                     8 * ii + 4 * g);
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv);
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * sc[e]);
         *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(r, 4 * dt + ii) + 8 * g) = w;
       }
+    const float mfix = MODE == kModeFp8 ? st.m_run[b] - kP8Log2 : st.m_run[b];   // FP8 sums 2^8 p
     if (p.lse != nullptr && g == 0 && q0 + r < Lq)
-      p.lse[(int64_t)h * Tq + qa + q0 + r] = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
+      p.lse[(int64_t)h * Tq + qa + q0 + r] = (mfix + __builtin_amdgcn_logf(lt)) * kLn2;
   }
   __syncthreads();
   constexpr int OCH = QB * 32 * C::CPR;      // 16-byte chunks of the wave's block
@@ -1274,6 +1422,119 @@ __global__ void __launch_bounds__(kMergeThreads) pfa_merge_kernel(MergeParams m)
 }
 
 // ---------------------------------------------------------------------------------
+// V quantiser of the FP8 P.V variant.  The FPS Attention slides (tool.lu deck on
+// accelerating multimodal generation, slides 35-38) quantise V per channel.  Here every
+// (segment, head, channel) gets the power-of-two scale 2^e, e the smallest integer with
+// max|V| 2^-e <= 448 (not below -126), and the codes are V 2^-e rounded to e4m3 (nearest
+// even).  Scaling by a power of two is exact, so the codes do not depend on the precision
+// of the arithmetic, and a segment's scales depend on its own tokens only.  Four launches:
+// zero the per-(segment, head, channel) maxima (held in v_scale as float bits), maxima
+// (order-independent atomic max of non-negative floats, so the result is deterministic),
+// codes, and finally the scales over the maxima.  All HBM-bound.
+// ---------------------------------------------------------------------------------
+constexpr int kQuantThreads = 256;
+constexpr int kQuantTokens = 64;   // tokens per thread in the maxima pass
+
+struct QuantParams {
+  const __bf16* v;
+  const int32_t* cu;
+  uint8_t* v8;
+  float* v_scale;   // [num_seqs, heads, d]: maxima (float bits) during the call, then scales
+  int num_seqs;
+  int heads;
+  int d;
+};
+
+// segment of row t: the last s with cu[s] <= t, skipping empty segments (cu[s+1] > t)
+__device__ __forceinline__ int segment_of(const int32_t* cu, int n, int64_t t) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ int v8_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int E;
+  const float m = __builtin_frexpf(amax, &E);   // amax = m 2^E, 0.5 <= m < 1
+  const int e = m <= 0.875f ? E - 9 : E - 8;    // 448 = 0.875 * 2^9
+  return e < -126 ? -126 : e;
+}
+
+__global__ void __launch_bounds__(kQuantThreads) pfa_v8_zero_kernel(QuantParams q) {
+  const int64_t n = (int64_t)q.num_seqs * q.heads * q.d;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kQuantThreads)
+    reinterpret_cast<uint32_t*>(q.v_scale)[i] = 0u;
+}
+
+__global__ void __launch_bounds__(kQuantThreads) pfa_v8_amax_kernel(QuantParams q) {
+  const int64_t T = q.cu[q.num_seqs];
+  const int cpt = q.heads * q.d / 8;                      // 16-byte chunks per token
+  const int64_t items = (T > 0 ? (T + kQuantTokens - 1) / kQuantTokens : 0) * cpt;
+  for (int64_t it = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kQuantThreads) {
+    const int64_t t0 = it / cpt * kQuantTokens;
+    const int j = (int)(it % cpt);
+    const int64_t t1 = t0 + kQuantTokens < T ? t0 + kQuantTokens : T;
+    int seg = segment_of(q.cu, q.num_seqs, t0);
+    int64_t seg_end = q.cu[seg + 1];
+    float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto flush = [&]() {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (mx[e] > 0.f) atomicMax(dst + e, __float_as_uint(mx[e]));
+    };
+    for (int64_t t = t0; t < t1; ++t) {
+      if (t >= seg_end) {
+        flush();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = 0.f;
+        while (q.cu[seg + 1] <= t) ++seg;
+        seg_end = q.cu[seg + 1];
+      }
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(q.v + t * cpt * 8 + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[e]));
+    }
+    flush();
+  }
+}
+
+__global__ void __launch_bounds__(kQuantThreads) pfa_v8_codes_kernel(QuantParams q) {
+  const int64_t T = q.cu[q.num_seqs];
+  const int cpt = q.heads * q.d / 8;
+  const int64_t items = (T > 0 ? T : 0) * cpt;
+  for (int64_t it = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; it < items;
+       it += (int64_t)gridDim.x * kQuantThreads) {
+    const int64_t t = it / cpt;
+    const int j = (int)(it % cpt);
+    const int seg = segment_of(q.cu, q.num_seqs, t);
+    const uint32_t* am = reinterpret_cast<const uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(q.v + t * cpt * 8 + 8 * j);
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf((float)x[e], -v8_exponent(__uint_as_float(am[e])));
+    int lo = 0, hi = 0;
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+    *reinterpret_cast<u32x2*>(q.v8 + t * cpt * 8 + 8 * j) = u32x2{(uint32_t)lo, (uint32_t)hi};
+  }
+}
+
+__global__ void __launch_bounds__(kQuantThreads) pfa_v8_scale_kernel(QuantParams q) {
+  const int64_t n = (int64_t)q.num_seqs * q.heads * q.d;
+  for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * kQuantThreads)
+    q.v_scale[i] = __builtin_ldexpf(1.0f, v8_exponent(q.v_scale[i]));
+}
+
+// ---------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------
 struct Variant {
@@ -1293,7 +1554,7 @@ Variant make_variant() {
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 8;  // head_dim 64, 128 x the four kernel modes
+constexpr int kVariants = 10;  // head_dim 64, 128 x the five kernel modes
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 std::atomic<int> g_bwd_occ[kMaxDevices][2][2];   // [device][head_dim 64 / 128][dK-dV / dQ]
@@ -1335,6 +1596,7 @@ Variant variant_for(int head_dim, int mode) {
   return mode == kModeCross  ? variant_of<kModeCross>(head_dim)
        : mode == kModeQkv    ? variant_of<kModeQkv>(head_dim)
        : mode == kModeSparse ? variant_of<kModeSparse>(head_dim)
+       : mode == kModeFp8    ? variant_of<kModeFp8>(head_dim)
                              : variant_of<kModeSelf>(head_dim);
 }
 
@@ -1611,6 +1873,78 @@ PFA_API int pfa_check_block_layout(const int32_t* cu_host, int num_seqs, int max
     }
   }
   return PFA_OK;
+}
+
+PFA_API int pfa_quantize_v_fp8(const void* v, const int32_t* cu_seqlens, int num_seqs, int heads,
+                               int head_dim, void* v8, float* v_scale, hipStream_t stream) {
+  if (v == nullptr || cu_seqlens == nullptr || v8 == nullptr || v_scale == nullptr) return PFA_ERR_NULL;
+  if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  const void* ins[2] = {v, cu_seqlens};
+  for (const void* in : ins)
+    if (in == v8 || in == static_cast<const void*>(v_scale)) return PFA_ERR_ALIAS;
+  if (v8 == static_cast<const void*>(v_scale)) return PFA_ERR_ALIAS;
+  if (misaligned16(v) || (reinterpret_cast<uintptr_t>(v8) & 7) != 0 || (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0)
+    return PFA_ERR_ALIGN;
+  if ((int64_t)heads * head_dim > kMaxRowElems || (int64_t)num_seqs * heads * head_dim > INT32_MAX)
+    return PFA_ERR_SIZE;
+  int dev = 0, cus = 0;
+  const int rc = device_cus(&dev, &cus);
+  if (rc != PFA_OK) return rc;
+  QuantParams qp;
+  qp.v = static_cast<const __bf16*>(v);
+  qp.cu = cu_seqlens;
+  qp.v8 = static_cast<uint8_t*>(v8);
+  qp.v_scale = v_scale;
+  qp.num_seqs = num_seqs;
+  qp.heads = heads;
+  qp.d = head_dim;
+  void* args[] = {&qp};
+  const void* fns[4] = {reinterpret_cast<const void*>(&pfa_v8_zero_kernel),
+                        reinterpret_cast<const void*>(&pfa_v8_amax_kernel),
+                        reinterpret_cast<const void*>(&pfa_v8_codes_kernel),
+                        reinterpret_cast<const void*>(&pfa_v8_scale_kernel)};
+  const unsigned grids[4] = {(unsigned)cus, (unsigned)cus * 8, (unsigned)cus * 8, (unsigned)cus};
+  for (int i = 0; i < 4; ++i)
+    if (hipLaunchKernel(fns[i], dim3(grids[i]), dim3(kQuantThreads), args, 0, stream) != hipSuccess)
+      return PFA_ERR_LAUNCH;
+  return PFA_OK;
+}
+
+PFA_API int pfa_varlen_fwd_fp8pv(const void* q, const void* k, const void* v8, const float* v_scale,
+                                 const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
+                                 int head_dim, float scale, void* out, float* lse, hipStream_t stream) {
+  // ---- argument checks: all before any HIP runtime call
+  if (q == nullptr || k == nullptr || v8 == nullptr || v_scale == nullptr || cu_seqlens == nullptr ||
+      out == nullptr)
+    return PFA_ERR_NULL;
+  if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (max_seqlen < 1) return PFA_ERR_MAX_SEQLEN;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
+  const void* ins[5] = {q, k, v8, v_scale, cu_seqlens};
+  for (const void* in : ins)
+    if (in == out || (lse != nullptr && in == static_cast<const void*>(lse))) return PFA_ERR_ALIAS;
+  if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
+  if (misaligned16(v8) || misaligned16(v_scale)) return PFA_ERR_ALIGN;
+  if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
+
+  Params prm{};
+  prm.q = static_cast<const __bf16*>(q);
+  prm.k = static_cast<const __bf16*>(k);
+  prm.v = static_cast<const __bf16*>(k);   // unused by this mode
+  prm.cu_q = cu_seqlens;
+  prm.cu_k = cu_seqlens;
+  prm.out = static_cast<__bf16*>(out);
+  prm.lse = lse;
+  prm.num_seqs = num_seqs;
+  prm.heads = heads;
+  prm.c = scale * kLog2e;
+  prm.v8 = static_cast<const uint8_t*>(v8);
+  prm.v_scale = v_scale;
+  return launch_fwd(prm, kModeFp8, max_seqlen, head_dim, stream);
 }
 
 PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,

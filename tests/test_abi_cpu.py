@@ -28,6 +28,7 @@ def declared_symbols():
 def test_header_declares_the_abi():
     assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv",
                                        "pfa_varlen_fwd_blocksparse", "pfa_check_block_layout",
+                                       "pfa_quantize_v_fp8", "pfa_varlen_fwd_fp8pv",
                                        "pfa_varlen_bwd", "pfa_attn_merge",
                                        "pfa_check_cu_seqlens", "pfa_status_string"}
 
@@ -184,6 +185,41 @@ def test_block_layout_validator():
     with pytest.raises(PfaError) as e:
         pfa_check_block_layout(cu, 200, 2, 1, np.zeros(5, np.int32), i)
     assert e.value.status == -8                    # cu_seqlens has a segment over max_seqlen
+
+
+def _quant(lib, v=16, cu=32, num_seqs=1, heads=2, head_dim=64, v8=48, v_scale=64):
+    return lib.pfa_quantize_v_fp8(v, cu, num_seqs, heads, head_dim, v8, v_scale, None)
+
+
+def _fp8(lib, q=16, k=32, v8=48, v_scale=64, cu=80, num_seqs=1, max_seqlen=1, heads=2, head_dim=128,
+         scale=1.0, out=96, lse=112):
+    return lib.pfa_varlen_fwd_fp8pv(q, k, v8, v_scale, cu, num_seqs, max_seqlen, heads, head_dim, scale,
+                                    out, lse, None)
+
+
+def test_fp8_argument_checks_run_before_any_hip_call(lib):
+    for name in ("v", "cu", "v8", "v_scale"):
+        assert _quant(lib, **{name: None}) == -1, name
+    assert _quant(lib, num_seqs=0) == -2
+    assert _quant(lib, heads=0) == -3
+    assert _quant(lib, head_dim=96) == -5
+    assert _quant(lib, v8=16) == -7
+    assert _quant(lib, v_scale=48) == -7
+    assert _quant(lib, v=24) == -12                   # v not 16-byte aligned
+    assert _quant(lib, v8=52) == -12
+    assert _quant(lib, v_scale=66) == -12
+    assert _quant(lib, num_seqs=2**20, heads=2**10) == -11
+    for name in ("q", "k", "v8", "v_scale", "cu", "out"):
+        assert _fp8(lib, **{name: None}) == -1, name
+    assert _fp8(lib, num_seqs=0) == -2
+    assert _fp8(lib, heads=0) == -3
+    assert _fp8(lib, max_seqlen=0) == -4
+    assert _fp8(lib, head_dim=32) == -5
+    assert _fp8(lib, scale=0.0) == -6
+    assert _fp8(lib, out=48) == -7
+    assert _fp8(lib, lse=64) == -7
+    assert _fp8(lib, v8=56) == -12
+    assert _fp8(lib, heads=2**17, head_dim=128) == -11
 
 
 def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):

@@ -1,0 +1,126 @@
+"""GPU parity of the FP8 P.V variant: the V quantiser (pfa_quantize_v_fp8) bit for bit
+against the oracle's, and the forward (pfa_varlen_fwd_fp8pv) against (a) exact attention on
+the dequantised V within the per-element bound of the FP8 weights, and (b) the oracle's
+emulation of the blocked FP8 steps, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+import pfa_workloads as W
+from tests._gpu import KERNEL_ALLOWANCE, LSE_ABS, bf16_half_ulp, from_dev_bf16, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# kernel vs the oracle's blocked FP8 steps: the bf16 output rounding (~1.7e-3 relative RMS)
+# plus fp32 arithmetic and the rare weight that sits on an e4m3 rounding boundary and rounds
+# the other way; the FP8 weights themselves move O by ~2e-2 relative RMS, so a kernel that
+# rounded the weights differently would fail this by a wide margin
+EMUL_REL_RMS = 4e-3
+
+
+def _quantize(wl, label):
+    import torch
+    from packed_varlen_flash_amd import pfa_quantize_v_fp8
+    say(f"[gpu] pfa_quantize_v_fp8 {label}: segs={wl.num_seqs} T={wl.total_tokens} H={wl.heads} d={wl.head_dim}")
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda")
+    v8, vs = pfa_quantize_v_fp8(to_dev(wl.v), cu)
+    torch.cuda.synchronize()
+    return v8, vs, cu
+
+
+def _run(wl, label, q_bits=None, rows=None, check_emulation=True):
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd_fp8pv
+    q_bits = wl.q if q_bits is None else q_bits
+    v8, vs, cu = _quantize(wl, label)
+    codes, scales = oracle.quantize_v_fp8(wl.v, wl.cu_seqlens)
+    np.testing.assert_array_equal(v8.cpu().numpy(), codes)
+    np.testing.assert_array_equal(vs.cpu().numpy().astype(np.float64), scales)
+    say(f"[gpu] pfa_varlen_fwd_fp8pv {label}")
+    out, lse = pfa_varlen_fwd_fp8pv(to_dev(q_bits), to_dev(wl.k), v8, vs, cu, wl.max_seqlen, wl.scale)
+    torch.cuda.synchronize()
+    o = W.bf16_to_f64(from_dev_bf16(out))
+    lse = lse.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        o, lse = o[rows], lse[:, rows]
+    vd = oracle.dequantize_v_fp8(codes, scales, wl.cu_seqlens)
+    o_ex, l_ex = oracle.varlen_fwd(W.bf16_to_f64(q_bits), W.bf16_to_f64(wl.k), vd, wl.cu_seqlens,
+                                   wl.scale, rows=rows)
+    bound = oracle.fp8pv_error_bound(q_bits, wl.k, codes, scales, wl.cu_seqlens, wl.scale, rows=rows)
+    err = np.abs(o - o_ex)
+    allow = bound + bf16_half_ulp(np.abs(o_ex) + bound) + KERNEL_ALLOWANCE
+    worst = float((err - allow).max())
+    say(f"[parity] {label}: max|err| vs exact {err.max():.3e} (bound up to {bound.max():.3e}), "
+        f"worst excess {worst:.3e}, LSE {np.abs(lse - l_ex).max():.3e}")
+    assert worst <= 0.0
+    assert float(np.abs(lse - l_ex).max()) <= LSE_ABS
+    if check_emulation:
+        o_em, _ = oracle.varlen_fwd_fp8pv_blocked(q_bits, wl.k, codes, scales, wl.cu_seqlens, wl.scale,
+                                                  rows=rows)
+        rr = float(np.sqrt(((o - o_em) ** 2).sum() / (o_em ** 2).sum()))
+        rr_ex = float(np.sqrt(((o_em - o_ex) ** 2).sum() / (o_ex ** 2).sum()))
+        say(f"[parity] {label}: relRMS vs the FP8 steps {rr:.3e} (the steps vs exact: {rr_ex:.3e})")
+        assert rr <= EMUL_REL_RMS
+    return o, lse
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_packs_full(seed):
+    rng = np.random.default_rng(400 + seed)
+    lengths = W.random_lengths(rng, int(rng.integers(1, 7)), 900)
+    if sum(lengths) == 0:
+        lengths[0] = 1
+    wl = W.make(lengths, 3, 64 if seed % 2 else 128, seed=400 + seed)
+    _run(wl, f"seed={seed} L={wl.lengths} d={wl.head_dim}")
+
+
+def test_sharp_heads_and_tile_boundaries_full():
+    wl = W.make([1, 64, 65, 255, 256, 257, 513], 3, 128, seed=410)
+    q = W.bf16_bits((W.bf16_to_f64(wl.q) * 3.0).astype(np.float32))
+    _run(wl, "sharp x3, tile boundaries", q_bits=q)
+
+
+def test_c3_sampled():
+    wl = W.generate("C3")
+    rows = W.sample_rows(wl.cu_seqlens, stride=61, edge=64, full_upto=0)
+    _run(wl, f"C3 sampled {len(rows)} rows", rows=rows)
+
+
+def test_pack_invariance_and_poison_isolation_bitwise():
+    import torch
+    from packed_varlen_flash_amd import pfa_quantize_v_fp8, pfa_varlen_fwd_fp8pv
+    wl = W.make([300, 17, 700], 2, 128, seed=411)
+    a, b = int(wl.cu_seqlens[1]), int(wl.cu_seqlens[2])
+
+    def run(q, k, v, cu_np, maxlen):
+        cu = torch.from_numpy(np.asarray(cu_np, np.int32)).to("cuda")
+        v8, vs = pfa_quantize_v_fp8(to_dev(v), cu)
+        out, lse = pfa_varlen_fwd_fp8pv(to_dev(q), to_dev(k), v8, vs, cu, maxlen, wl.scale)
+        torch.cuda.synchronize()
+        return from_dev_bf16(out), lse.cpu().numpy(), v8.cpu().numpy()
+
+    o, l, v8 = run(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.max_seqlen)
+    o1, l1, v81 = run(wl.q[a:b], wl.k[a:b], wl.v[a:b], [0, b - a], b - a)
+    np.testing.assert_array_equal(o[a:b], o1)
+    np.testing.assert_array_equal(l[:, a:b], l1)
+    np.testing.assert_array_equal(v8[a:b], v81)
+    q, k, v = wl.q.copy(), wl.k.copy(), wl.v.copy()
+    for arr, val in ((q, 0x7FC0), (k, 0x7F80), (v, 0x7FC0)):        # NaN, Inf, NaN elsewhere
+        arr[:a] = val
+        arr[b:] = val
+    o2, l2, _ = run(q, k, v, wl.cu_seqlens, wl.max_seqlen)
+    np.testing.assert_array_equal(o2[a:b], o[a:b])
+    np.testing.assert_array_equal(l2[:, a:b], l[:, a:b])
+
+
+def test_binding_checks():
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd_fp8pv
+    wl = W.make([40], 1, 64, seed=412)
+    q = to_dev(wl.q)
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda")
+    v8 = torch.zeros((40, 1, 64), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        pfa_varlen_fwd_fp8pv(q, q, v8, torch.ones((2, 1, 64), device="cuda"), cu, 40)   # wrong scale shape
+    with pytest.raises(ValueError):
+        pfa_varlen_fwd_fp8pv(q, q, v8.to(torch.int8), torch.ones((1, 1, 64), device="cuda"), cu, 40)

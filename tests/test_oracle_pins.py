@@ -802,9 +802,11 @@ def test_e4m3_codes_round_trip():
 def test_v_scale_exponent_is_the_smallest_that_fits():
     rng = np.random.default_rng(51)
     amax = np.concatenate([np.exp(rng.uniform(-20, 20, 5000)), [448.0, 449.0, 224.0, 1.0, 0.875 * 2 ** 9]])
+    # (none of these is small enough for the -126 floor)
     e = oracle.v_scale_exponent(amax)
     assert np.all(amax * 2.0 ** -e <= 448.0) and np.all(amax * 2.0 ** -(e - 1) > 448.0)
     assert list(oracle.v_scale_exponent(np.array([448.0, 449.0, 0.0]))) == [0, 1, 0]
+    assert list(oracle.v_scale_exponent(np.array([2.0 ** -120, 2.0 ** -133]))) == [-126, -126]
 
 
 def test_quantize_v_per_segment_channel():
