@@ -64,7 +64,6 @@ constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters uncons
 constexpr float kRescaleSlack = 0.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct Params {
   const __bf16* q;
@@ -259,8 +258,7 @@ struct TileState {
   bf16x8 qr[QB][C::KSTEP];       // Q fragments (B operand of K Q^T)
   f32x16 o[QB][C::DT];           // O^T accumulators
   float m_run[QB];               // running max (base-2 scaled)
-  float l_run[QB];               // row sum of the fp32 weights (for the LSE)
-  float l_rnd[QB];               // row sum of the bf16 weights (normalises O)
+  float l_run[QB];               // row sum of the fp32 weights (normalises O, gives the LSE)
 };
 
 // K operand fragments of one 32-key sub-block: kst points at the sub-block's first row;
@@ -355,7 +353,6 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
       const float a = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
       st.m_run[b] = m_new;
       st.l_run[b] *= a;
-      st.l_rnd[b] *= a;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -364,13 +361,13 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
   }
 }
 
-// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
-// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of bf16-rounded weights
-// can carry up to 2^-8 relative error, 3.9e-3, into the LSE of a sharp row).  l_rnd adds the bf16
-// weights the PV product actually uses and normalises O: the rounding of each weight then
-// enters numerator and denominator alike, which measurably tightens the worst output error
-// on sharp rows.  Both sums chain straight into their running values (one add, resp. one
-// bf16 dot of a weight pair, per step), with no partial sums to seed or combine.
+// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and the
+// row sum l_run of the fp32 weights, which normalises O and gives the LSE (a sum of the
+// bf16-rounded weights could carry up to 2^-8 relative error, 3.9e-3, into the LSE of a
+// sharp row).  With the exact running maximum each row's largest weight is 1 and exact in
+// bf16, so normalising by the rounded weights' sum instead gains no accuracy; it cost 16
+// dot products per stage in a loop bound by vector issue.  The sum chains straight into
+// its running value, with no partial sums to seed or combine.
 template <int D, int QB>
 __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
                                              bf16x8 (&pb)[QB][2], float c) {
@@ -384,7 +381,6 @@ __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 
       st.l_run[b] += e0;
       st.l_run[b] += e1;
       const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-      st.l_rnd[b] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, st.l_rnd[b], false);
       pb[b][i >> 3][i & 7] = pr[0];
       pb[b][i >> 3][(i & 7) + 1] = pr[1];
     }
@@ -623,7 +619,6 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     }
     st.m_run[b] = -INFINITY;
     st.l_run[b] = 0.f;
-    st.l_rnd[b] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -722,7 +717,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
   __syncthreads();   // every wave has left the ring
 
-  // ---- epilogue: O = acc / l_rnd in bf16 (round to nearest even), LSE = ln2 * (m + log2
+  // ---- epilogue: O = acc / l_run in bf16 (round to nearest even), LSE = ln2 * (m + log2
   // l_run).  O goes out through LDS: each wave writes its (QB*32) x D block into the free
   // ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
   // consecutive rows, so 16 lanes store 256 contiguous bytes instead of every store
@@ -732,10 +727,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = partner_sum(st.l_run[b]);
-    // FP8: O is normalised by the unrounded weights (l_run), the bf16 paths by the sum of
-    // the rounded ones (l_rnd)
-    const float lr = MODE == kModeFp8 ? lt : partner_sum(st.l_rnd[b]);
-    const float inv = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // no keys: O = 0 (and LSE = -inf)
     const int r = b * 32 + n32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
