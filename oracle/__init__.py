@@ -403,15 +403,30 @@ def dequantize_v_fp8(codes, scales, cu_seqlens):
     return e4m3_decode(codes) * scales[seg]
 
 
+def _retained_blocks(layout, L, s, h, H, qb, block_q, block_k):
+    """Key blocks of query block qb of segment s, head h, in visiting order: every block in
+    order without a layout, else the listed ones inside the segment (list order)."""
+    nkb = -(-L // block_k)
+    if layout is None:
+        return list(range(nkb))
+    listed = list(layout[h if len(layout) == H else 0][s][qb])
+    if len(set(listed)) != len(listed):
+        raise ValueError(f"repeated key block in segment {s}, head {h}, query block {qb}")
+    return [J for J in listed if 0 <= J < nkb]
+
+
 def varlen_fwd_fp8pv_blocked(q, k, v_codes, v_scales, cu_seqlens, scale: float, block: int = 64,
-                             quantize: bool = True, rows=None):
+                             quantize: bool = True, rows=None, layout=None, block_q: int = 256):
     """The blocked online softmax (GigaPath-Flash page, section 3.2) with the P.V product in
     FP8, in fp64: per query row and 64-key block in order, the running maximum m (base 2)
     is raised to the block's maximum, accumulator and row sum are rescaled, the weights
     w = 2^8 2^(s log2(e) - m) are summed unrounded into l and rounded to e4m3 for the
     product with the e4m3 values of V; finally O = acc * scale_V / l and
     LSE = ln 2 (m - 8 + log2 l).  quantize=False keeps w unrounded (then the result is
-    plain attention on the dequantised V)."""
+    plain attention on the dequantised V).  With a block-sparse ``layout`` (see
+    varlen_fwd_blocksparse; query blocks of block_q rows) only the listed key blocks are
+    visited, in list order: the FPS Attention combination of sliding tiles and FP8.  A row
+    with no retained key gets O = 0 and LSE = -inf."""
     q = widen_bf16(q) if np.asarray(q).dtype == np.uint16 else np.asarray(q, np.float64)
     k = widen_bf16(k) if np.asarray(k).dtype == np.uint16 else np.asarray(k, np.float64)
     v8 = e4m3_decode(v_codes)
@@ -422,16 +437,17 @@ def varlen_fwd_fp8pv_blocked(q, k, v_codes, v_scales, cu_seqlens, scale: float, 
     out = np.zeros((want.shape[0], H, d))
     lse = np.full((H, want.shape[0]), -np.inf)
     c = scale / math.log(2.0)
-    for s in np.unique(seg_of):
+    qblk = (want - cu[seg_of]) // block_q if layout is not None else np.zeros_like(want)
+    for s, qb in sorted(set(zip(seg_of.tolist(), qblk.tolist()))):
         a, L = int(cu[s]), int(cu[s + 1] - cu[s])
-        sel = np.nonzero(seg_of == s)[0]
+        sel = np.nonzero((seg_of == s) & (qblk == qb))[0]
         qi = want[sel]
         for h in range(H):
             m = np.full(sel.shape[0], -np.inf)
             l = np.zeros(sel.shape[0])
             acc = np.zeros((sel.shape[0], d))
-            for b0 in range(0, L, block):
-                kk = np.arange(a + b0, a + min(b0 + block, L))
+            for J in _retained_blocks(layout, L, s, h, H, qb, block_q, block):
+                kk = np.arange(a + J * block, a + min((J + 1) * block, L))
                 sc = (q[qi, h] @ k[kk, h].T) * c
                 m_new = np.maximum(m, sc.max(axis=1))
                 alpha = np.where(np.isneginf(m), 0.0, np.exp2(m - m_new))
@@ -440,13 +456,16 @@ def varlen_fwd_fp8pv_blocked(q, k, v_codes, v_scales, cu_seqlens, scale: float, 
                 wq = e4m3_round(w) if quantize else w
                 acc = acc * alpha[:, None] + wq @ v8[kk, h]
                 m = m_new
-            out[sel, h] = acc * v_scales[s, h][None, :] / l[:, None]
-            lse[h, sel] = math.log(2.0) * (m - P_SCALE_LOG2 + np.log2(l))
+            has = l > 0
+            out[sel[has], h] = acc[has] * v_scales[s, h][None, :] / l[has, None]
+            lse[h, sel[has]] = math.log(2.0) * (m[has] - P_SCALE_LOG2 + np.log2(l[has]))
     return out, lse
 
 
-def fp8pv_error_bound(q, k, v_codes, v_scales, cu_seqlens, scale: float, rows=None):
-    """Per-element bound on |O_fp8 - O| for O the exact attention on the dequantised V:
+def fp8pv_error_bound(q, k, v_codes, v_scales, cu_seqlens, scale: float, rows=None, layout=None,
+                      block_q: int = 256, block_k: int = 64):
+    """Per-element bound on |O_fp8 - O| for O the exact attention on the dequantised V
+    (over the retained keys when a block-sparse ``layout`` is given):
     O_fp8 = sum_j w8_j V_j / sum_j w_j with the same unrounded normaliser, and each e4m3
     weight is within max(2^-4 w_j, 2^-10) of w_j (half a step: relative 2^-4 for normal
     values, 2^-10 absolute below 2^-6).  With w_j = 2^8 p_j 2^(m_stage - M) <= 2^8 p_j,
@@ -458,14 +477,19 @@ def fp8pv_error_bound(q, k, v_codes, v_scales, cu_seqlens, scale: float, rows=No
     T, H, d = q.shape
     want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
     seg_of = np.searchsorted(cu[1:], want, side="right")
+    qblk = (want - cu[seg_of]) // block_q if layout is not None else np.zeros_like(want)
     bound = np.zeros((want.shape[0], H, d))
-    for s in np.unique(seg_of):
-        a, b = int(cu[s]), int(cu[s + 1])
-        sel = np.nonzero(seg_of == s)[0]
+    for s, qb in sorted(set(zip(seg_of.tolist(), qblk.tolist()))):
+        a, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        sel = np.nonzero((seg_of == s) & (qblk == qb))[0]
         for h in range(H):
-            sc = scale * (q[want[sel], h] @ k[a:b, h].T)
+            blocks = _retained_blocks(layout, L, s, h, H, qb, block_q, block_k)
+            if not blocks:
+                continue
+            kk = np.concatenate([np.arange(a + J * block_k, a + min((J + 1) * block_k, L)) for J in blocks])
+            sc = scale * (q[want[sel], h] @ k[kk, h].T)
             p = np.exp(sc - sc.max(axis=1, keepdims=True))
-            bound[sel, h] = (2.0 ** -4 * (p @ vd[a:b, h]) + 2.0 ** -18 * vd[a:b, h].sum(axis=0)) \
+            bound[sel, h] = (2.0 ** -4 * (p @ vd[kk, h]) + 2.0 ** -18 * vd[kk, h].sum(axis=0)) \
                 / p.sum(axis=1, keepdims=True)
     return bound
 

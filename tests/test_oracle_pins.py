@@ -861,3 +861,33 @@ def test_fp8pv_blocked_steps_stay_within_the_bound(qk_scale):
     np.testing.assert_allclose(o2, o[rows], rtol=0, atol=1e-13)
     np.testing.assert_allclose(oracle.fp8pv_error_bound(q, w.k, codes, scales, w.cu_seqlens, w.scale,
                                                         rows=rows), bound[rows], rtol=1e-12, atol=0)
+
+
+def test_fps_blocked_fp8_steps_over_block_lists():
+    """FPS Attention = sliding-tile block lists + FP8 P.V (tool.lu deck, slides 35-38): the
+    blocked FP8 steps visit only the listed key blocks.  Every block listed gives the dense
+    steps; unrounded weights give exact block-sparse attention on the dequantised V; with
+    rounding the result stays within the bound over the retained keys; an empty list gives
+    a zero row and LSE = -inf."""
+    rng = np.random.default_rng(55)
+    w = W.make([700, 90, 300], 2, 64, seed=56)
+    codes, scales = oracle.quantize_v_fp8(w.v, w.cu_seqlens)
+    full = [[[list(range(-(-L // 64))) for _ in range(-(-L // 256))] for L in w.lengths]]
+    o_d, l_d = oracle.varlen_fwd_fp8pv_blocked(w.q, w.k, codes, scales, w.cu_seqlens, w.scale)
+    o_f, l_f = oracle.varlen_fwd_fp8pv_blocked(w.q, w.k, codes, scales, w.cu_seqlens, w.scale, layout=full)
+    np.testing.assert_allclose(o_f, o_d, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_f, l_d, rtol=0, atol=1e-13)
+    lay = W.random_layout(rng, w.lengths, 2, density=0.5)
+    lay[1][0][1] = []                                               # head 1, rows 256..511: no keys
+    vd = oracle.dequantize_v_fp8(codes, scales, w.cu_seqlens)
+    o_x, l_x = oracle.varlen_fwd_blocksparse(W.bf16_to_f64(w.q), W.bf16_to_f64(w.k), vd, w.cu_seqlens,
+                                             w.scale, lay)
+    o_u, l_u = oracle.varlen_fwd_fp8pv_blocked(w.q, w.k, codes, scales, w.cu_seqlens, w.scale,
+                                               quantize=False, layout=lay)
+    np.testing.assert_allclose(o_u, o_x, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_u[np.isfinite(l_x)], l_x[np.isfinite(l_x)], rtol=0, atol=1e-12)
+    assert np.all(np.isneginf(l_u[1, 256:512])) and np.all(o_u[256:512, 1] == 0)
+    o_q, l_q = oracle.varlen_fwd_fp8pv_blocked(w.q, w.k, codes, scales, w.cu_seqlens, w.scale, layout=lay)
+    bound = oracle.fp8pv_error_bound(w.q, w.k, codes, scales, w.cu_seqlens, w.scale, layout=lay)
+    err = np.abs(o_q - o_x)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-13) and (err / np.maximum(bound, 1e-300)).max() > 0.1
