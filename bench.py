@@ -18,6 +18,7 @@ row sample of the same workload.
     python bench.py --op qkv             # fused [T,3,H,d] input with 2-D RoPE, same pack
     python bench.py --op sparse          # block-sparse band layout (+-1024 tokens), same pack
     python bench.py --op fp8pv           # P.V in FP8 (V quantised per segment/head/channel)
+    python bench.py --op fps             # FPS attention: the band layout with P.V in FP8
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -396,6 +397,96 @@ def bench_qkv(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_fps(args):
+    """FPS Attention: the band layout of --op sparse with P.V in FP8.  Counted work is the
+    listed work (4·d·allowed pairs); the roofline takes half of it at the bf16 rate and
+    half at the fp8 rate.  The bf16 block-sparse and the dense forward are timed beside it."""
+    import torch
+    import oracle
+    from packed_varlen_flash_amd import (block_layout_csr, pfa_quantize_v_fp8, pfa_varlen_fwd,
+                                         pfa_varlen_fwd_blocksparse, pfa_varlen_fwd_blocksparse_fp8pv)
+    wl = W.generate(args.config, seed=args.seed)
+    T, H, d = wl.total_tokens, wl.heads, wl.head_dim
+    lay = W.band_layout(wl.lengths, radius=args.band)
+    kv_ptr_np, kv_idx_np, lh = block_layout_csr(lay, wl.lengths, wl.max_seqlen)
+    pairs = W.layout_pairs(lay, wl.lengths, H)
+    flop = 4.0 * d * pairs
+    dev = torch.device("cuda:0")
+    up = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = up(wl.q), up(wl.k), up(wl.v)
+    cu = torch.from_numpy(wl.cu_seqlens).to(dev)
+    kv_ptr, kv_idx = torch.from_numpy(kv_ptr_np).to(dev), torch.from_numpy(kv_idx_np).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    v8, vs = pfa_quantize_v_fp8(v, cu, stream=stream)
+
+    def step():
+        pfa_varlen_fwd_blocksparse_fp8pv(q, k, v8, vs, cu, wl.max_seqlen, kv_ptr, kv_idx, lh, wl.scale,
+                                         out=out, lse=lse, stream=stream)
+
+    def step_sparse_bf16():
+        pfa_varlen_fwd_blocksparse(q, k, v, cu, wl.max_seqlen, kv_ptr, kv_idx, lh, wl.scale, out=out,
+                                   lse=lse, stream=stream)
+
+    def step_dense():
+        pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
+
+    ms_dense, _ = timed(step_dense, stream, args.steps, args.warmup)
+    ms_sp, _ = timed(step_sparse_bf16, stream, args.steps, args.warmup)
+    ms, kms = timed(step, stream, args.steps, args.warmup)
+    peak = 2.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(1234)
+        codes, scales = oracle.quantize_v_fp8(wl.v, wl.cu_seqlens)
+        n = 512
+        for attempt in range(3):
+            rows = np.sort(rng.choice(T, size=n, replace=False))
+            t0 = time.perf_counter()
+            o_em, l_em = oracle.varlen_fwd_fp8pv_blocked(wl.q, wl.k, codes, scales, wl.cu_seqlens,
+                                                         wl.scale, rows=rows, layout=lay)
+            dt = time.perf_counter() - t0
+            if n == T or dt > args.cpu_budget / 2:
+                break
+            n = int(min(T, n * args.cpu_budget / max(dt, 1e-3)))
+        seg = np.searchsorted(wl.cu_seqlens[1:], rows, side="right")
+        nk = 0
+        for r, sg in zip(rows, seg):
+            a, L = int(wl.cu_seqlens[sg]), int(wl.lengths[sg])
+            nk += sum(min(64, L - J * 64) for J in lay[0][sg][(int(r) - a) // 256])
+        sflop = 4.0 * d * H * nk
+        o = W.bf16_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16)[rows])
+        dd = o - o_em
+        parity = {"rows": int(n), "rel_rms_vs_fp8_steps": float(np.sqrt((dd * dd).sum() / (o_em * o_em).sum())),
+                  "max_abs_err_vs_fp8_steps": float(np.abs(dd).max()),
+                  "lse_max_abs_err": float(np.abs(lse.cpu().numpy()[:, rows] - l_em).max())}
+        from threadpoolctl import threadpool_info
+        blas = [x["num_threads"] for x in threadpool_info() if x.get("user_api") == "blas"]
+        cpu = {"value": sflop / dt / 1e12, "unit": "TFLOP/s", "cores": max(blas) if blas else 1,
+               "kind": "oracle",
+               "sample": f"{n} uniformly drawn query rows of {wl.name} through the blocked FP8 steps "
+                         f"over the band lists (numpy fp64): {sflop / 1e9:.1f} GFLOP in {dt:.1f} s"}
+    achieved = flop / (kms * 1e-3) / 1e12
+    rec = {"metric": "FPS attention (block-sparse + FP8 P.V) TFLOP/s (4·d·listed pairs), 1 GPU",
+           "value": round(flop / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16 QK, e4m3 PV",
+           "data": "synthetic (seeded N(0,1) bf16 Q/K/V; V quantised by the library; band layout)",
+           "config": {"workload": f"{describe(wl)}; each 256-query block attends the 64-key blocks "
+                                  f"within +-{args.band} tokens; V in e4m3",
+                      "segments": list(wl.lengths), "heads": H, "head_dim": d, "listed_pairs": pairs,
+                      "density": round(flop / wl.flops, 4), "flop_per_step": flop, "seed": args.seed},
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 1),
+                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                        "frac_of_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "kernel_ms": round(kms, 5)},
+           "sparse_bf16_ms": round(ms_sp, 5), "dense_bf16_ms": round(ms_dense, 5),
+           "speedup_vs_dense": round(ms_dense / ms, 3),
+           "cpu_baseline": cpu, "parity_on_sample": parity}
+    print(json.dumps(rec), flush=True)
+
+
 def bench_sparse(args):
     """Block-sparse forward on the same pack: every 256-query block attends the 64-key blocks
     of a +-radius band around it (a sliding-tile layout).  Counted work is the listed work,
@@ -589,7 +680,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
-    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv", "sparse", "fp8pv"])
+    ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv", "sparse", "fp8pv", "fps"])
     ap.add_argument("--band", type=int, default=1024, help="band radius (tokens) for --op sparse")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -618,6 +709,9 @@ def main():
         return
     if args.op == "fp8pv":
         bench_fp8pv(args)
+        return
+    if args.op == "fps":
+        bench_fps(args)
         return
     if args.op == "bwd":
         bench_bwd(args)

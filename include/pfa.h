@@ -262,6 +262,23 @@ PFA_API int pfa_varlen_fwd_fp8pv(const void* q, const void* k, const void* v8, c
                                  hipStream_t stream);
 
 /*
+ * pfa_varlen_fwd_blocksparse_fp8pv -- FPS Attention: block-sparse tile lists with P.V in FP8.
+ *
+ * The FPS Attention slides (tool.lu deck, slides 35-38) combine sliding-tile sparsity with
+ * FP8 attention. This is pfa_varlen_fwd_blocksparse (the same CSR lists, block sizes,
+ * limits and empty-row convention) with the FP8 arithmetic of pfa_varlen_fwd_fp8pv (V
+ * from pfa_quantize_v_fp8, e4m3 weights scaled by 2^8, O normalised by the unrounded
+ * weights). The running maximum visits the listed blocks in list order. Arguments and
+ * errors are the union of the two calls'.
+ */
+PFA_API int pfa_varlen_fwd_blocksparse_fp8pv(const void* q, const void* k, const void* v8,
+                                             const float* v_scale, const int32_t* cu_seqlens,
+                                             int num_seqs, int max_seqlen, int heads,
+                                             int head_dim, float scale, const int32_t* kv_ptr,
+                                             const int32_t* kv_idx, int nnz, int layout_heads,
+                                             void* out, float* lse, hipStream_t stream);
+
+/*
  * pfa_attn_merge -- combine two results for the same queries over disjoint key sets.
  *
  * If (o_a, lse_a) is attention over key set A and (o_b, lse_b) over key set B, the

@@ -17,6 +17,7 @@ from . import _lib
 __all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv", "pfa_varlen_bwd",
            "pfa_varlen_fwd_blocksparse", "block_layout_csr", "pfa_check_block_layout",
            "SPARSE_BLOCK_Q", "SPARSE_BLOCK_K", "pfa_quantize_v_fp8", "pfa_varlen_fwd_fp8pv",
+           "pfa_varlen_fwd_blocksparse_fp8pv",
            "pfa_attn_merge",
            "pfa_check_cu_seqlens",
            "pfa_status_string", "PfaError", "LIB_PATH"]
@@ -343,6 +344,52 @@ def pfa_varlen_fwd_fp8pv(q, k, v8, v_scale, cu_seqlens, max_seqlen: int, scale: 
     rc = _lib.load().pfa_varlen_fwd_fp8pv(
         _ptr(q), _ptr(k), _ptr(v8), _ptr(v_scale), _ptr(cu_seqlens), n, int(max_seqlen), H, d,
         float(scale), _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return out, lse
+
+
+def pfa_varlen_fwd_blocksparse_fp8pv(q, k, v8, v_scale, cu_seqlens, max_seqlen: int, kv_ptr, kv_idx,
+                                     layout_heads: int = 1, scale: float | None = None, out=None,
+                                     lse=None, want_lse: bool = True, stream=None):
+    """FPS Attention: block-sparse lists (as pfa_varlen_fwd_blocksparse) with P.V in FP8 (as
+    pfa_varlen_fwd_fp8pv).  Returns (out bf16 [T, H, d], lse fp32 [H, T] or None)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k)):
+        _check_bf16(name, t, torch)
+    if k.shape != q.shape:
+        raise ValueError("q and k must have the same shape")
+    _check_table("cu_seqlens", cu_seqlens, torch)
+    _check_table("kv_ptr", kv_ptr, torch)
+    if kv_idx.numel() > 0:
+        _check_table("kv_idx", kv_idx, torch)
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    if v8.dtype != torch.uint8 or tuple(v8.shape) != (T, H, d) or not v8.is_contiguous() or not v8.is_cuda:
+        raise ValueError("v8 must be a contiguous uint8 CUDA tensor [T, H, d]")
+    if (v_scale.dtype != torch.float32 or tuple(v_scale.shape) != (n, H, d) or not v_scale.is_contiguous()
+            or not v_scale.is_cuda):
+        raise ValueError("v_scale must be a contiguous fp32 CUDA tensor [num_seqs, H, d]")
+    rows = n * int(layout_heads) * (-(-int(max_seqlen) // SPARSE_BLOCK_Q))
+    if kv_ptr.numel() != rows + 1:
+        raise ValueError(f"kv_ptr must have {rows + 1} entries for this max_seqlen and layout_heads")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_fwd_blocksparse_fp8pv(
+        _ptr(q), _ptr(k), _ptr(v8), _ptr(v_scale), _ptr(cu_seqlens), n, int(max_seqlen), H, d,
+        float(scale), _ptr(kv_ptr), _ptr(kv_idx) if kv_idx.numel() > 0 else None, int(kv_idx.numel()),
+        int(layout_heads), _ptr(out), _ptr(lse), ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise PfaError(rc)
     return out, lse

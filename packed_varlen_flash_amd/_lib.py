@@ -28,6 +28,9 @@ _SIGNATURES = {
                            [ctypes.c_void_p] * 3),
     "pfa_varlen_fwd_fp8pv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
                              [ctypes.c_float] + [ctypes.c_void_p] * 3),
+    "pfa_varlen_fwd_blocksparse_fp8pv": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 4 +
+                                         [ctypes.c_float] + [ctypes.c_void_p] * 2 +
+                                         [ctypes.c_int] * 2 + [ctypes.c_void_p] * 3),
     "pfa_attn_merge": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),

@@ -102,6 +102,9 @@ constexpr int kModeCross = 1;
 constexpr int kModeQkv = 2;
 constexpr int kModeSparse = 3;   // one table; each query tile reads only its listed key blocks
 constexpr int kModeFp8 = 4;      // one table; P.V in FP8 (e4m3 weights and V)
+constexpr int kModeSparseFp8 = 5;   // both: listed key blocks, P.V in FP8
+constexpr bool mode_sparse(int mode) { return mode == kModeSparse || mode == kModeSparseFp8; }
+constexpr bool mode_fp8(int mode) { return mode == kModeFp8 || mode == kModeSparseFp8; }
 // FP8 weights: w = 2^8 p with p = 2^(s log2 e - m) in (0, 1], so w <= 256 < 448 (the
 // largest e4m3 value) and the factor is folded into the exponent.
 constexpr float kP8Log2 = 8.0f;
@@ -558,11 +561,11 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   const __bf16* qbase = p.q + (int64_t)qa * q_rs + head_off;
   const __bf16* kbase = p.k + (int64_t)ka * k_rs + head_off;
   const __bf16* vbase = p.v + (int64_t)ka * v_rs + head_off;
-  const uint8_t* v8base = MODE == kModeFp8 ? p.v8 + (int64_t)ka * rs + head_off : nullptr;
+  const uint8_t* v8base = mode_fp8(MODE) ? p.v8 + (int64_t)ka * rs + head_off : nullptr;
   const int q0 = qt * C::BM + wave * (QB * 32);
   int ns = (Lk + SK - 1) / SK;             // LDS stages (0 when the key segment is empty)
   const float c = p.c;
-  if constexpr (MODE == kModeSparse) {
+  if constexpr (mode_sparse(MODE)) {
     // The tile's list, compacted by wave 0 into LDS: entries outside the segment's key
     // blocks are dropped, the rest keep their order.  ns becomes the number kept.  (The
     // previous tile's last barrier retired every reader of the old list.)
@@ -592,7 +595,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
   // first key of stage i: consecutive 64-key stages, or the listed blocks in list order
   auto stage_key = [&](int i) {
-    if constexpr (MODE == kModeSparse) return __builtin_amdgcn_readfirstlane(s_blk[i]) * SK;
+    if constexpr (mode_sparse(MODE)) return __builtin_amdgcn_readfirstlane(s_blk[i]) * SK;
     else return i * SK;
   };
 
@@ -629,7 +632,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   int koff[C::KSTEP], voff[C::DT];
 #pragma unroll
   for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
-  if constexpr (MODE == kModeFp8) {
+  if constexpr (mode_fp8(MODE)) {
     // transposed e4m3 reads: lane i16 supplies row i16/2 (keys 4g + 0..3, then 8 + 4g +
     // 0..3) and half i16 & 1 of the 16 channels 32dt + 16hh ..; v8_operand adds 16q rows
     const int r = i16 >> 1;
@@ -657,7 +660,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   for (int i = 0; i < C::CPT; ++i) {
     const int P = (wave * C::CPT + i) * 64 + lane;
     src_k[i] = logical_src<D, true>(P, kbytes);
-    if constexpr (MODE == kModeFp8) {
+    if constexpr (mode_fp8(MODE)) {
       if (i < C::CPT8) src_v[i] = logical_src8<D>((wave * C::CPT8 + i) * 64 + lane, (int)rs);
     } else {
       src_v[i] = logical_src<D, false>(P, vbytes);
@@ -672,7 +675,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16, src_k[i], 0, 0, 0);
-    if constexpr (MODE == kModeFp8) {
+    if constexpr (mode_fp8(MODE)) {
       __amdgpu_buffer_rsrc_t r8 = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(v8base + (int64_t)kb * rs), 0, rows * (int)rs, kRsrcFlags);
       vdst += wave * C::CPT8 * 1024;
@@ -699,7 +702,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   for (int s = 0; s < ns; s += 2) {
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    if constexpr (MODE == kModeFp8)
+    if constexpr (mode_fp8(MODE))
       stage_body_fp8<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
                                 issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
     else
@@ -708,7 +711,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     if (s + 1 >= ns) break;
     __builtin_amdgcn_s_waitcnt(kWaitVmem);
     __syncthreads();
-    if constexpr (MODE == kModeFp8)
+    if constexpr (mode_fp8(MODE))
       stage_body_fp8<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
                                 issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
     else
@@ -735,7 +738,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
       for (int ii = 0; ii < 4; ++ii) {
         // this lane's channels 32dt + 8ii + 4g + e; FP8 dequantises V per channel here
         f32x4 sc = {inv, inv, inv, inv};
-        if constexpr (MODE == kModeFp8)
+        if constexpr (mode_fp8(MODE))
           sc = inv * *reinterpret_cast<const f32x4*>(p.v_scale + ((int64_t)seg * p.heads + h) * D + 32 * dt +
                                                      8 * ii + 4 * g);
         bf16x4 w;
@@ -743,7 +746,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
         for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * sc[e]);
         *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(r, 4 * dt + ii) + 8 * g) = w;
       }
-    const float mfix = MODE == kModeFp8 ? st.m_run[b] - kP8Log2 : st.m_run[b];   // FP8 sums 2^8 p
+    const float mfix = mode_fp8(MODE) ? st.m_run[b] - kP8Log2 : st.m_run[b];   // FP8 sums 2^8 p
     if (p.lse != nullptr && g == 0 && q0 + r < Lq)
       p.lse[(int64_t)h * Tq + qa + q0 + r] = (mfix + __builtin_amdgcn_logf(lt)) * kLn2;
   }
@@ -1539,14 +1542,14 @@ struct Variant {
 template <int D, int QB, int NW, int SK, int WPE, int MODE>
 Variant make_variant() {
   using C = Tile<D, QB, NW, SK>;
-  static_assert(MODE != kModeSparse || (C::BM == PFA_SPARSE_BLOCK_Q && SK == PFA_SPARSE_BLOCK_K),
+  static_assert(!mode_sparse(MODE) || (C::BM == PFA_SPARSE_BLOCK_Q && SK == PFA_SPARSE_BLOCK_K),
                 "the block-sparse layout's blocks are the kernel's query tile and key stage");
   return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, MODE>), C::BM,
-                 C::THREADS, C::LDS_BYTES + (MODE == kModeSparse ? kSparseLdsBytes : 0)};
+                 C::THREADS, C::LDS_BYTES + (mode_sparse(MODE) ? kSparseLdsBytes : 0)};
 }
 
 constexpr int kMaxDevices = 64;
-constexpr int kVariants = 10;  // head_dim 64, 128 x the five kernel modes
+constexpr int kVariants = 12;  // head_dim 64, 128 x the six kernel modes
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 std::atomic<int> g_bwd_occ[kMaxDevices][2][2];   // [device][head_dim 64 / 128][dK-dV / dQ]
@@ -1589,6 +1592,7 @@ Variant variant_for(int head_dim, int mode) {
        : mode == kModeQkv    ? variant_of<kModeQkv>(head_dim)
        : mode == kModeSparse ? variant_of<kModeSparse>(head_dim)
        : mode == kModeFp8    ? variant_of<kModeFp8>(head_dim)
+       : mode == kModeSparseFp8 ? variant_of<kModeSparseFp8>(head_dim)
                              : variant_of<kModeSelf>(head_dim);
 }
 
@@ -1937,6 +1941,51 @@ PFA_API int pfa_varlen_fwd_fp8pv(const void* q, const void* k, const void* v8, c
   prm.v8 = static_cast<const uint8_t*>(v8);
   prm.v_scale = v_scale;
   return launch_fwd(prm, kModeFp8, max_seqlen, head_dim, stream);
+}
+
+PFA_API int pfa_varlen_fwd_blocksparse_fp8pv(const void* q, const void* k, const void* v8,
+                                             const float* v_scale, const int32_t* cu_seqlens,
+                                             int num_seqs, int max_seqlen, int heads, int head_dim,
+                                             float scale, const int32_t* kv_ptr, const int32_t* kv_idx,
+                                             int nnz, int layout_heads, void* out, float* lse,
+                                             hipStream_t stream) {
+  // ---- argument checks: all before any HIP runtime call
+  if (q == nullptr || k == nullptr || v8 == nullptr || v_scale == nullptr || cu_seqlens == nullptr ||
+      out == nullptr || kv_ptr == nullptr || (kv_idx == nullptr && nnz > 0))
+    return PFA_ERR_NULL;
+  if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
+  if (heads < 1) return PFA_ERR_HEADS;
+  if (max_seqlen < 1) return PFA_ERR_MAX_SEQLEN;
+  if (head_dim != 64 && head_dim != 128) return PFA_ERR_HEAD_DIM;
+  if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
+  if (nnz < 0 || (layout_heads != 1 && layout_heads != heads)) return PFA_ERR_LAYOUT;
+  const void* ins[7] = {q, k, v8, v_scale, cu_seqlens, kv_ptr, kv_idx};
+  for (const void* in : ins)
+    if (in != nullptr && (in == out || (lse != nullptr && in == static_cast<const void*>(lse))))
+      return PFA_ERR_ALIAS;
+  if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
+  if (misaligned16(v8) || misaligned16(v_scale)) return PFA_ERR_ALIGN;
+  if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
+  if ((int64_t)max_seqlen > (int64_t)kSparseMaxBlocks * PFA_SPARSE_BLOCK_K) return PFA_ERR_SIZE;
+
+  Params prm{};
+  prm.q = static_cast<const __bf16*>(q);
+  prm.k = static_cast<const __bf16*>(k);
+  prm.v = static_cast<const __bf16*>(k);   // unused by this mode
+  prm.cu_q = cu_seqlens;
+  prm.cu_k = cu_seqlens;
+  prm.out = static_cast<__bf16*>(out);
+  prm.lse = lse;
+  prm.num_seqs = num_seqs;
+  prm.heads = heads;
+  prm.c = scale * kLog2e;
+  prm.kv_ptr = kv_ptr;
+  prm.kv_idx = kv_idx;
+  prm.nnz = nnz;
+  prm.layout_heads = layout_heads;
+  prm.v8 = static_cast<const uint8_t*>(v8);
+  prm.v_scale = v_scale;
+  return launch_fwd(prm, kModeSparseFp8, max_seqlen, head_dim, stream);
 }
 
 PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,

@@ -29,6 +29,7 @@ def test_header_declares_the_abi():
     assert set(declared_symbols()) == {"pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv",
                                        "pfa_varlen_fwd_blocksparse", "pfa_check_block_layout",
                                        "pfa_quantize_v_fp8", "pfa_varlen_fwd_fp8pv",
+                                       "pfa_varlen_fwd_blocksparse_fp8pv",
                                        "pfa_varlen_bwd", "pfa_attn_merge",
                                        "pfa_check_cu_seqlens", "pfa_status_string"}
 
@@ -220,6 +221,26 @@ def test_fp8_argument_checks_run_before_any_hip_call(lib):
     assert _fp8(lib, lse=64) == -7
     assert _fp8(lib, v8=56) == -12
     assert _fp8(lib, heads=2**17, head_dim=128) == -11
+
+
+def _fps(lib, q=16, k=32, v8=48, v_scale=64, cu=80, num_seqs=1, max_seqlen=1, heads=2, head_dim=128,
+         scale=1.0, kv_ptr=96, kv_idx=112, nnz=1, layout_heads=1, out=128, lse=144):
+    return lib.pfa_varlen_fwd_blocksparse_fp8pv(q, k, v8, v_scale, cu, num_seqs, max_seqlen, heads,
+                                                head_dim, scale, kv_ptr, kv_idx, nnz, layout_heads,
+                                                out, lse, None)
+
+
+def test_fps_argument_checks_run_before_any_hip_call(lib):
+    for name in ("q", "k", "v8", "v_scale", "cu", "out", "kv_ptr", "kv_idx"):
+        assert _fps(lib, **{name: None}) == -1, name
+    assert _fps(lib, kv_idx=None, nnz=0) != -1            # no entries, no index array needed
+    assert _fps(lib, num_seqs=0) == -2
+    assert _fps(lib, layout_heads=3) == -13
+    assert _fps(lib, nnz=-2) == -13
+    assert _fps(lib, out=112) == -7
+    assert _fps(lib, lse=48) == -7
+    assert _fps(lib, v_scale=68) == -12
+    assert _fps(lib, max_seqlen=65537) == -11
 
 
 def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):
