@@ -899,7 +899,11 @@ __global__ void __launch_bounds__(kRopeThreads) pfa_rope_k_kernel(RopeParams r) 
 // reads take explicit per-lane offsets for each 16-row step and 8-row half, since that
 // swizzle does not keep a constant pattern 8 rows apart.
 // ---------------------------------------------------------------------------------
-constexpr int kBwdNW = 4;                  // waves per workgroup (one per SIMD)
+// waves per workgroup (one per SIMD).  dK/dV holds two accumulators and the stationary K
+// and V fragments (419 registers at d = 128), so one workgroup fills a CU; dQ loads its
+// two operand sets one after the other and fits 256 registers, so two workgroups share a
+// CU (its few spills are per-item offsets, reloaded outside the stage loop).
+constexpr int kBwdNW = 4;
 constexpr int kBwdRows = kBwdNW * 32;      // keys (dK/dV) or queries (dQ) per work item
 constexpr int kBwdStage = 64;              // rows per streamed stage
 
@@ -1238,7 +1242,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
 
 // ---- dQ
 template <int D>
-__global__ void __launch_bounds__(kWave * kBwdNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kWave * kBwdNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pfa_bwd_dq_kernel(BwdParams p) {
   using C = BwdTile<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1325,16 +1329,24 @@ pfa_bwd_dq_kernel(BwdParams p) {
         const char* vj = vst + j * 32 * D * 2;
         f32x16 sc, dp;
         {
-          bf16x8 ka[C::KSTEP], va[C::KSTEP];
-          k_operands<D>(kj, koff, ka);
-          k_operands<D>(vj, koff, va);
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
+          {
+            bf16x8 ka[C::KSTEP];
+            k_operands<D>(kj, koff, ka);
 #pragma unroll
-          for (int t = 0; t < C::KSTEP; ++t) {
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], qr[t], sc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], dr[t], dp, 0, 0, 0);
+            for (int t = 0; t < C::KSTEP; ++t)
+              sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], qr[t], sc, 0, 0, 0);
           }
+          __builtin_amdgcn_sched_barrier(0);   // one operand set live at a time
+          {
+            bf16x8 va[C::KSTEP];
+            k_operands<D>(vj, koff, va);
+#pragma unroll
+            for (int t = 0; t < C::KSTEP; ++t)
+              dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[t], dr[t], dp, 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
         // element i holds key s*64 + j*32 + 8(i/4) + 4g + i%4 for this lane's query
         const int key0 = s * kBwdStage + j * 32;
@@ -1345,13 +1357,20 @@ pfa_bwd_dq_kernel(BwdParams p) {
           const float pv = key < L ? __builtin_amdgcn_exp2f(fmaf(sc[i], p.c, nl)) : 0.f;
           dsp[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl));
         }
-        bf16x8 ta[2][C::DT];
-        t_operands<D>(kj, toff, ta);                 // K^T
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
+        for (int cc = 0; cc < 2; ++cc) {             // K^T, one 16-key half at a time
+          bf16x8 ta[C::DT];
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt) {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kj + toff[cc][0][dt]));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(kj + toff[cc][1][dt]));
+            ta[dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
 #pragma unroll
           for (int dt = 0; dt < C::DT; ++dt)
-            dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[cc][dt], dsp[cc], dqt[dt], 0, 0, 0);
+            dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[dt], dsp[cc], dqt[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     __syncthreads();   // every wave has left the ring
