@@ -11,7 +11,9 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "pfa_fwd.hip")
+CSRC = os.path.join(HERE, "csrc")
+# forward (all kernel modes), backward, and the merge / V quantiser; pfa_common.h is shared
+SRCS = [os.path.join(CSRC, n) for n in ("pfa_fwd.hip", "pfa_bwd.hip", "pfa_aux.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpfa.so")
 ARCH = "gfx950"
@@ -27,9 +29,9 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-fvisibility=hidden", "-fno-honor-nans", "-I", INCLUDE,
+           "-fvisibility=hidden", "-fno-honor-nans", "-I", INCLUDE, "-I", CSRC,
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           SRC, "-o", tmp]
+           *SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

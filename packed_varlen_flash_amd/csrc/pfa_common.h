@@ -1,0 +1,152 @@
+// pfa_common.h -- definitions shared by the library's kernels (gfx950): vector types,
+// launch constants, the LDS swizzles of K/V stage tiles, the device-side longest-first
+// scheduler, the K operand reads, and the host-side device query.  Everything sits in an
+// anonymous namespace, so each translation unit has its own copy.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "pfa.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int kWave = 64;
+constexpr int kHalf = 64;        // keys per softmax step (two 32-key sub-blocks)
+constexpr int kStages = 2;       // LDS ring depth (stages)
+constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
+constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
+constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Largest row stride (elements) of any input: 64 rows of it, in bytes, must stay within
+// the 32-bit offsets of a buffer resource.
+constexpr int64_t kMaxRowElems = int64_t(1) << 23;
+
+// LDS layout of a K or V stage: 16-byte chunks, row-major (row = key), with the chunk
+// index XOR-swizzled inside each 256-byte line so the two read patterns are free of bank
+// conflicts: K operand reads (16 lanes = 16 consecutive rows, one logical chunk) and
+// transposed V reads (4 consecutive rows x 64 bytes per 32 lanes).
+__device__ __forceinline__ int swz_k(int line) { return line & 15; }
+__device__ __forceinline__ int swz_v(int line) { return (line & 3) << 2; }
+
+// byte offset of logical (row, chunk) within a stage
+template <int D, bool IS_K>
+__device__ __forceinline__ int phys_off(int row, int chunk) {
+  const int P = row * (D / 8) + chunk;
+  const int line = P >> 4;
+  const int sw = IS_K ? swz_k(line) : swz_v(line);
+  return ((line << 4) | ((P & 15) ^ sw)) << 4;
+}
+
+// logical byte offset (row * row_bytes + chunk * 16) of the chunk stored at physical
+// chunk position P; the XOR swizzle is its own inverse
+template <int D, bool IS_K>
+__device__ __forceinline__ int logical_src(int P, int row_bytes) {
+  const int line = P >> 4;
+  const int sw = IS_K ? swz_k(line) : swz_v(line);
+  const int Pl = (line << 4) | ((P & 15) ^ sw);
+  return (Pl / (D / 8)) * row_bytes + (Pl % (D / 8)) * 16;
+}
+
+// ---------------------------------------------------------------------------------
+// Device-side scheduler: decode cu_seqlens into a longest-first list of work items.
+// ---------------------------------------------------------------------------------
+// Sorted mode (num_seqs <= kSortMax): s_order[r] = segment of rank r (key length, i.e.
+// the work per query tile, descending; ties by index), s_prefix[r] = first item of rank
+// r; a segment has heads * ceil(query length / BM) items, ordered head-major,
+// query-tile-minor.  Returns the item count.
+template <int BM, int THREADS>
+__device__ int build_schedule(const int32_t* cu_q, const int32_t* cu_k, int n, int heads,
+                              int* s_len, int* s_order, int* s_prefix) {
+  const int tid = threadIdx.x;
+  for (int s = tid; s < n; s += THREADS) {
+    int L = cu_k[s + 1] - cu_k[s];
+    s_len[s] = L > 0 ? L : 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < n; s += THREADS) {
+    const int L = s_len[s];
+    int rank = 0;
+    for (int t = 0; t < n; ++t) {
+      const int Lt = s_len[t];
+      rank += (Lt > L) || (Lt == L && t < s);
+    }
+    s_order[rank] = s;
+  }
+  __syncthreads();
+  // items per rank, then an inclusive Hillis-Steele scan in place (n <= kSortMax)
+  for (int r = tid; r < n; r += THREADS) {
+    const int sg = s_order[r];
+    int Lq = cu_q[sg + 1] - cu_q[sg];
+    Lq = Lq > 0 ? Lq : 0;
+    s_prefix[r + 1] = heads * ((Lq + BM - 1) / BM);
+  }
+  if (tid == 0) s_prefix[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < n; off <<= 1) {
+    int add[kSortMax / THREADS];
+#pragma unroll
+    for (int j = 0; j < kSortMax / THREADS; ++j) {
+      const int r = tid + j * THREADS;
+      add[j] = (r < n && r >= off) ? s_prefix[r + 1 - off] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSortMax / THREADS; ++j) {
+      const int r = tid + j * THREADS;
+      if (r < n) s_prefix[r + 1] += add[j];
+    }
+    __syncthreads();
+  }
+  return s_prefix[n];
+}
+
+// K operand fragments of one 32-key sub-block: kst points at the sub-block's first row;
+// koff[t] is this lane's byte offset of (row n32, chunk 2t+g).
+template <int D>
+__device__ __forceinline__ void k_operands(const char* kst, const int (&koff)[D / 16],
+                                           bf16x8 (&a)[D / 16]) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
+}
+
+// ---- host side
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];   // compute units per device, 0 until queried
+
+// compute units of the current device (cached; a race only recomputes the same value)
+int device_cus(int* dev_out, int* cus_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_DEVICE;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return PFA_ERR_DEVICE;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  *dev_out = dev;
+  *cus_out = cus;
+  return PFA_OK;
+}
+
+inline bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
+}  // namespace
