@@ -71,6 +71,7 @@ __global__ void __launch_bounds__(kMergeThreads) pfa_merge_kernel(MergeParams m)
 // ---------------------------------------------------------------------------------
 constexpr int kQuantThreads = 256;
 constexpr int kQuantTokens = 64;   // tokens per thread in the maxima pass
+constexpr int kQuantUnroll = 8;    // loads in flight per thread; tokens per thread in the codes pass
 
 struct QuantParams {
   const __bf16* v;
@@ -116,51 +117,78 @@ __global__ void __launch_bounds__(kQuantThreads) pfa_v8_amax_kernel(QuantParams 
     const int64_t t0 = it / cpt * kQuantTokens;
     const int j = (int)(it % cpt);
     const int64_t t1 = t0 + kQuantTokens < T ? t0 + kQuantTokens : T;
+    const __bf16* src = q.v + 8 * j;
     int seg = segment_of(q.cu, q.num_seqs, t0);
-    int64_t seg_end = q.cu[seg + 1];
-    float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    auto flush = [&]() {
+    int64_t t = t0;
+    while (t < t1) {
+      // the run of tokens of this item inside segment seg
+      const int64_t seg_end = q.cu[seg + 1];
+      const int64_t run_end = seg_end < t1 ? seg_end : t1;
+      float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (; t + kQuantUnroll <= run_end; t += kQuantUnroll) {   // independent loads in flight
+        bf16x8 x[kQuantUnroll];
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u) x[u] = *reinterpret_cast<const bf16x8*>(src + (t + u) * cpt * 8);
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[u][e]));
+      }
+      for (; t < run_end; ++t) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + t * cpt * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[e]));
+      }
       uint32_t* dst = reinterpret_cast<uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         if (mx[e] > 0.f) atomicMax(dst + e, __float_as_uint(mx[e]));
-    };
-    for (int64_t t = t0; t < t1; ++t) {
-      if (t >= seg_end) {
-        flush();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx[e] = 0.f;
-        while (q.cu[seg + 1] <= t) ++seg;
-        seg_end = q.cu[seg + 1];
-      }
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(q.v + t * cpt * 8 + 8 * j);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[e]));
+      while (t < t1 && q.cu[seg + 1] <= t) ++seg;    // next non-empty segment
     }
-    flush();
   }
 }
 
 __global__ void __launch_bounds__(kQuantThreads) pfa_v8_codes_kernel(QuantParams q) {
   const int64_t T = q.cu[q.num_seqs];
   const int cpt = q.heads * q.d / 8;
-  const int64_t items = (T > 0 ? T : 0) * cpt;
+  const int64_t items = (T > 0 ? (T + kQuantUnroll - 1) / kQuantUnroll : 0) * cpt;
   for (int64_t it = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; it < items;
        it += (int64_t)gridDim.x * kQuantThreads) {
-    const int64_t t = it / cpt;
+    const int64_t t0 = it / cpt * kQuantUnroll;        // kQuantUnroll tokens of one chunk column
     const int j = (int)(it % cpt);
-    const int seg = segment_of(q.cu, q.num_seqs, t);
-    const uint32_t* am = reinterpret_cast<const uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(q.v + t * cpt * 8 + 8 * j);
-    float y[8];
+    const int n = T - t0 < kQuantUnroll ? (int)(T - t0) : kQuantUnroll;
+    bf16x8 x[kQuantUnroll];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf((float)x[e], -v8_exponent(__uint_as_float(am[e])));
-    int lo = 0, hi = 0;
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
-    lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
-    hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
-    *reinterpret_cast<u32x2*>(q.v8 + t * cpt * 8 + 8 * j) = u32x2{(uint32_t)lo, (uint32_t)hi};
+    for (int u = 0; u < kQuantUnroll; ++u)
+      if (u < n) x[u] = *reinterpret_cast<const bf16x8*>(q.v + (t0 + u) * cpt * 8 + 8 * j);
+    int seg = segment_of(q.cu, q.num_seqs, t0);
+    int64_t seg_end = q.cu[seg + 1];
+    int ex[8];
+    auto exponents = [&]() {
+      const uint32_t* am = reinterpret_cast<const uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ex[e] = v8_exponent(__uint_as_float(am[e]));
+    };
+    exponents();
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      if (u >= n) break;
+      const int64_t t = t0 + u;
+      if (t >= seg_end) {                          // the run crosses into the next segment(s)
+        while (q.cu[seg + 1] <= t) ++seg;
+        seg_end = q.cu[seg + 1];
+        exponents();
+      }
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf((float)x[u][e], -ex[e]);
+      int lo = 0, hi = 0;
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+      *reinterpret_cast<u32x2*>(q.v8 + t * cpt * 8 + 8 * j) = u32x2{(uint32_t)lo, (uint32_t)hi};
+    }
   }
 }
 
