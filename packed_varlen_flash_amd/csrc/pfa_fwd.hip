@@ -26,6 +26,10 @@
 //     O^T += V^T P^T; the V^T operand comes from row-major V in LDS through
 //     ds_read_b64_tr_b16 transposed loads.
 //   * exp is v_exp_f32 (base 2) with scale*log2(e) folded into one FMA per score.
+//   * one kernel template, six modes fixed at compile time: one segment table; separate
+//     query and key tables; q, k, v read through row strides from a fused projection
+//     output (q rotated on load); listed key blocks only; P.V in FP8; listed key blocks
+//     with P.V in FP8.  The modes share the tile routine and differ only where noted.
 #include <vector>
 
 #include "pfa_common.h"
