@@ -86,6 +86,7 @@ constexpr bool mode_fp8(int mode) { return mode == kModeFp8 || mode == kModeSpar
 // FP8 weights: w = 2^8 p with p = 2^(s log2 e - m) in (0, 1], so w <= 256 < 448 (the
 // largest e4m3 value) and the factor is folded into the exponent.
 constexpr float kP8Log2 = 8.0f;
+__device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // Block-sparse variant: a compacted copy of the tile's key-block list lives in LDS after
 // the schedule (count in the last slot), so segments are limited to this many key blocks.
 constexpr int kSparseMaxBlocks = 1024;
@@ -157,7 +158,8 @@ struct TileState {
   bf16x8 qr[QB][C::KSTEP];       // Q fragments (B operand of K Q^T)
   f32x16 o[QB][C::DT];           // O^T accumulators
   float m_run[QB];               // running max (base-2 scaled)
-  float l_run[QB];               // row sum of the fp32 weights (normalises O, gives the LSE)
+  float l_run[QB];               // row sum of the fp32 weights (gives the LSE; normalises FP8 O)
+  float l_rnd[QB];               // row sum of the bf16 weights (normalises bf16 O)
 };
 
 // S^T (keys x queries) = K Q^T for both 32-key sub-blocks of a stage, the two accumulator
@@ -243,6 +245,7 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
       const float a = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
       st.m_run[b] = m_new;
       st.l_run[b] *= a;
+      st.l_rnd[b] *= a;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -251,13 +254,15 @@ __device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0
   }
 }
 
-// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and the
-// row sum l_run of the fp32 weights, which normalises O and gives the LSE (a sum of the
-// bf16-rounded weights could carry up to 2^-8 relative error, 3.9e-3, into the LSE of a
-// sharp row).  With the exact running maximum each row's largest weight is 1 and exact in
-// bf16, so normalising by the rounded weights' sum instead gains no accuracy; it cost 16
-// dot products per stage in a loop bound by vector issue.  The sum chains straight into
-// its running value, with no partial sums to seed or combine.
+// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
+// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of bf16-rounded weights
+// can carry up to 2^-8 relative error, 3.9e-3, into the LSE of a sharp row).  l_rnd adds
+// the bf16 weights the PV product actually uses and normalises O: each weight's rounding
+// then enters numerator and denominator alike, so the error is sum_j dp_j (v_j - O) / l
+// rather than sum_j dp_j v_j / l.  That matters on rows with few keys and large, similar
+// values (|O| in [2, 4), where bf16 rounding of O already takes 2^-7 of the 1e-2 bar);
+// normalising by l_run there was measured past the bar.  Both sums chain straight into
+// their running values (one add, resp. one bf16 dot of a weight pair, per step).
 template <int D, int QB>
 __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
                                              bf16x8 (&pb)[QB][2], float c) {
@@ -271,6 +276,7 @@ __device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 
       st.l_run[b] += e0;
       st.l_run[b] += e1;
       const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+      st.l_rnd[b] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, st.l_rnd[b], false);
       pb[b][i >> 3][i & 7] = pr[0];
       pb[b][i >> 3][(i & 7) + 1] = pr[1];
     }
@@ -509,6 +515,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     }
     st.m_run[b] = -INFINITY;
     st.l_run[b] = 0.f;
+    st.l_rnd[b] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -607,8 +614,8 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   }
   __syncthreads();   // every wave has left the ring
 
-  // ---- epilogue: O = acc / l_run in bf16 (round to nearest even), LSE = ln2 * (m + log2
-  // l_run).  O goes out through LDS: each wave writes its (QB*32) x D block into the free
+  // ---- epilogue: O = acc / l_rnd (FP8: acc / l_run) in bf16 (round to nearest even),
+  // LSE = ln2 * (m + log2 l_run).  O goes out through LDS: each wave writes its (QB*32) x D block into the free
   // ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
   // consecutive rows, so 16 lanes store 256 contiguous bytes instead of every store
   // instruction touching 16-byte pieces of 32 different rows.
@@ -617,7 +624,8 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float lt = partner_sum(st.l_run[b]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;   // no keys: O = 0 (and LSE = -inf)
+    const float lr = mode_fp8(MODE) ? lt : partner_sum(st.l_rnd[b]);
+    const float inv = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
     const int r = b * 32 + n32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)

@@ -124,3 +124,10 @@ def test_binding_checks():
         pfa_varlen_fwd_fp8pv(q, q, v8, torch.ones((2, 1, 64), device="cuda"), cu, 40)   # wrong scale shape
     with pytest.raises(ValueError):
         pfa_varlen_fwd_fp8pv(q, q, v8.to(torch.int8), torch.ones((1, 1, 64), device="cuda"), cu, 40)
+
+
+def test_many_segments_unsorted_schedule():
+    rng = np.random.default_rng(413)
+    lengths = [int(x) for x in rng.integers(0, 200, size=650)]
+    wl = W.make(lengths, 2, 64, seed=413, name="650 segments")
+    _run(wl, "650 segments, unsorted schedule")

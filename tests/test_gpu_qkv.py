@@ -129,3 +129,14 @@ def test_without_lse_and_binding_checks():
         pfa_varlen_fwd_qkv(qkv, cu, wl.max_seqlen, rope_cos=c[:, :16], rope_sin=c[:, :16])
     with pytest.raises(ValueError):
         pfa_varlen_fwd_qkv(qkv[:, :2], cu, wl.max_seqlen)                   # not [T, 3, H, d]
+
+
+def test_many_segments_unsorted_schedule_with_rope():
+    rng = np.random.default_rng(35)
+    lengths = [int(x) for x in rng.integers(0, 200, size=600)]
+    wl = W.make(lengths, 2, 128, seed=35, name="600 segments")
+    cos, sin = W.rope_tables_2d(wl.lengths, 128)
+    qkv = W.fuse_qkv(wl.q, wl.k, wl.v)
+    ob, lse, _ = _run(wl, qkv, cos, sin, "600 segments, rope")
+    o_ref, l_ref = oracle.qkv_rope_fwd(qkv, wl.cu_seqlens, wl.scale, cos, sin)
+    assert_parity(compare(ob, lse, o_ref, l_ref), "qkv 600 segments")
