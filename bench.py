@@ -139,7 +139,6 @@ def timed(step, stream, steps, warmup):
 def bench_cross(args):
     """Separate query / key tables on a long-Q, short-KV pack: HBM is the roof."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import pfa_varlen_fwd_qk
     x = W.generate_cross(args.config, seed=args.seed)
     dev = torch.device("cuda:0")
@@ -158,6 +157,7 @@ def bench_cross(args):
     alg = x.total_q * x.heads * (4 * x.head_dim + 4) + x.total_k * x.heads * 4 * x.head_dim
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         rng = np.random.default_rng(1234)
         rows = np.sort(rng.choice(x.total_q, size=min(x.total_q, 4096), replace=False))
         t0 = time.perf_counter()
@@ -193,7 +193,6 @@ def bench_cross(args):
 def bench_merge(args):
     """(O, LSE) merge of two bf16 results at the Mage-Flow pack's shape: HBM-bound."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import pfa_attn_merge
     c = W.CONFIGS["C3"]
     T, H, d = sum(c.lengths), c.heads, c.head_dim
@@ -217,6 +216,7 @@ def bench_merge(args):
     alg = T * H * (3 * 2 * d + 3 * 4)
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         fa, fb = W.bf16_to_f64(o_a), W.bf16_to_f64(o_b)
         t0 = time.perf_counter()
         o_ref, l_ref = oracle.merge(fa, l_a.astype(np.float64), fb, l_b.astype(np.float64))
@@ -251,7 +251,6 @@ def bench_bwd(args):
     dK/dV, dQ).  Counted work 10*sum(L^2)*H*d (five L x L x d matmuls, the usual count);
     this design executes seven (S and dP are recomputed in each of the two passes)."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import pfa_varlen_bwd, pfa_varlen_fwd
     wl = W.generate(args.config, seed=args.seed)
     dev = torch.device("cuda:0")
@@ -275,6 +274,7 @@ def bench_bwd(args):
     executed = 3.5 * wl.flops
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         heads = [0, wl.heads - 1]
         sl = lambda a: np.ascontiguousarray(a[:, heads])
         t0 = time.perf_counter()
@@ -314,7 +314,6 @@ def bench_qkv(args):
     it, the same work without the fusion (separate contiguous q, k, v copies and RoPE in
     PyTorch ops, then the plain forward) is timed for comparison."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import pfa_varlen_fwd, pfa_varlen_fwd_qkv
     wl = W.generate(args.config, seed=args.seed)
     T, H, d = wl.total_tokens, wl.heads, wl.head_dim
@@ -354,6 +353,7 @@ def bench_qkv(args):
     rot_bytes = T * (4 * H * d + 4 * d)          # read k, both tables; write rotated k
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         rng = np.random.default_rng(1234)
         pilot = np.sort(rng.choice(T, size=24, replace=False))
         t0 = time.perf_counter()
@@ -402,7 +402,6 @@ def bench_fps(args):
     listed work (4·d·allowed pairs); the roofline takes half of it at the bf16 rate and
     half at the fp8 rate.  The bf16 block-sparse and the dense forward are timed beside it."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import (block_layout_csr, pfa_quantize_v_fp8, pfa_varlen_fwd,
                                          pfa_varlen_fwd_blocksparse, pfa_varlen_fwd_blocksparse_fp8pv)
     wl = W.generate(args.config, seed=args.seed)
@@ -438,6 +437,7 @@ def bench_fps(args):
     peak = 2.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         rng = np.random.default_rng(1234)
         codes, scales = oracle.quantize_v_fp8(wl.v, wl.cu_seqlens)
         n = 512
@@ -492,7 +492,6 @@ def bench_sparse(args):
     of a +-radius band around it (a sliding-tile layout).  Counted work is the listed work,
     4·d·(allowed query-key pairs summed over heads); the dense forward is timed beside it."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import block_layout_csr, pfa_varlen_fwd, pfa_varlen_fwd_blocksparse
     wl = W.generate(args.config, seed=args.seed)
     T, H, d = wl.total_tokens, wl.heads, wl.head_dim
@@ -520,6 +519,7 @@ def bench_sparse(args):
     ms, kms = timed(step, stream, args.steps, args.warmup)
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         rng = np.random.default_rng(1234)
         pilot = np.sort(rng.choice(T, size=48, replace=False))
         t0 = time.perf_counter()
@@ -584,7 +584,6 @@ def bench_fp8pv(args):
     attention kernel's roofline takes half the counted work at the bf16 rate and half at
     the fp8 rate (2 / (1/2.5 + 1/5) = 3.33 PFLOP/s)."""
     import torch
-    import oracle
     from packed_varlen_flash_amd import pfa_quantize_v_fp8, pfa_varlen_fwd, pfa_varlen_fwd_fp8pv
     wl = W.generate(args.config, seed=args.seed)
     T, H, d = wl.total_tokens, wl.heads, wl.head_dim
@@ -613,6 +612,7 @@ def bench_fp8pv(args):
     peak = 2.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / PEAK_FP8_TFLOPS)
     cpu = parity = None
     if not args.no_cpu_baseline:
+        import oracle   # the CPU-baseline leg only
         rng = np.random.default_rng(1234)
         t0 = time.perf_counter()
         codes, scales = oracle.quantize_v_fp8(wl.v, wl.cu_seqlens)
