@@ -1,5 +1,7 @@
 /*
- * pfa.h -- packed variable-length attention forward for AMD Instinct MI355X (gfx950).
+ * pfa.h -- packed variable-length attention for AMD Instinct MI355X (gfx950): the forward,
+ * its variants (separate query/key tables, fused QKV input with RoPE, block-sparse tile
+ * lists, FP8 P.V), the (O, LSE) merge and the backward.
  *
  * Several images' patch tokens are concatenated into one sequence and an int32 prefix
  * table cu_seqlens = [0, len0, len0+len1, ...] tells which rows belong to which image

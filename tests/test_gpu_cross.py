@@ -1,5 +1,7 @@
 """GPU parity of the separate-table forward (pfa_varlen_fwd_qk) and of the (O, LSE) merge
 (pfa_attn_merge) against the fp64 oracle, through the C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -166,3 +168,19 @@ def test_merge_of_two_key_halves_end_to_end():
     assert m["max_abs_small"] <= 1e-2 + extra
     assert m["rel_rms"] <= 4e-3 + 2.0 ** -8 / np.sqrt(3.0)
     assert m["lse_abs"] <= LSE_ABS
+
+
+def test_poison_in_other_segments_does_not_leak():
+    # NaN / Inf in the rows of other segments (queries and keys) leave segment 1 bitwise equal
+    x = W.make_cross([300, 257, 40], [90, 513, 7], 2, 128, seed=14, name="poison")
+    ob, lse = _run(x, "clean")
+    q, k, v = x.q.copy(), x.k.copy(), x.v.copy()
+    qa, qb = int(x.cu_q[1]), int(x.cu_q[2])
+    ka, kb = int(x.cu_k[1]), int(x.cu_k[2])
+    q[:qa] = q[qb:] = 0x7FC0
+    k[:ka] = k[kb:] = 0x7F80
+    v[:ka] = v[kb:] = 0x7FC0
+    y = dataclasses.replace(x, q=q, k=k, v=v)
+    ob2, lse2 = _run(y, "poisoned neighbours")
+    np.testing.assert_array_equal(ob2[qa:qb], ob[qa:qb])
+    np.testing.assert_array_equal(lse2[:, qa:qb], lse[:, qa:qb])

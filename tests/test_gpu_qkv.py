@@ -140,3 +140,17 @@ def test_many_segments_unsorted_schedule_with_rope():
     ob, lse, _ = _run(wl, qkv, cos, sin, "600 segments, rope")
     o_ref, l_ref = oracle.qkv_rope_fwd(qkv, wl.cu_seqlens, wl.scale, cos, sin)
     assert_parity(compare(ob, lse, o_ref, l_ref), "qkv 600 segments")
+
+
+def test_poison_in_other_segments_does_not_leak():
+    wl = W.make([300, 700, 90], 2, 128, seed=36)
+    cos, sin = W.rope_tables_2d(wl.lengths, 128)
+    qkv = W.fuse_qkv(wl.q, wl.k, wl.v)
+    ob, lse, _ = _run(wl, qkv, cos, sin, "clean")
+    a, b = int(wl.cu_seqlens[1]), int(wl.cu_seqlens[2])
+    bad = qkv.copy()
+    bad[:a] = 0x7FC0
+    bad[b:] = 0x7F80
+    ob2, lse2, _ = _run(wl, bad, cos, sin, "poisoned neighbours")
+    np.testing.assert_array_equal(ob2[a:b], ob[a:b])
+    np.testing.assert_array_equal(lse2[:, a:b], lse[:, a:b])

@@ -1,6 +1,8 @@
 """GPU parity of the block-sparse forward (pfa_varlen_fwd_blocksparse) against the fp64
 oracle, through the C ABI: each 256-query block of a segment attends only its listed
 64-key blocks, with the softmax renormalised over them."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -129,3 +131,18 @@ def test_many_segments_unsorted_schedule():
     wl = W.make(lengths, 2, 128, seed=315, name="700 segments")
     lay = W.random_layout(rng, wl.lengths, 1, density=0.7)
     _check(wl, lay, "700 segments, unsorted schedule")
+
+
+def test_poison_in_other_segments_does_not_leak():
+    wl = W.make([300, 700, 90], 2, 128, seed=316)
+    lay = W.band_layout(wl.lengths, radius=200)
+    ob, lse = _run(wl, lay, "clean")
+    a, b = int(wl.cu_seqlens[1]), int(wl.cu_seqlens[2])
+    q, k, v = wl.q.copy(), wl.k.copy(), wl.v.copy()
+    for arr, val in ((q, 0x7FC0), (k, 0x7F80), (v, 0x7FC0)):
+        arr[:a] = val
+        arr[b:] = val
+    w2 = dataclasses.replace(wl, q=q, k=k, v=v)
+    ob2, lse2 = _run(w2, lay, "poisoned neighbours")
+    np.testing.assert_array_equal(ob2[a:b], ob[a:b])
+    np.testing.assert_array_equal(lse2[:, a:b], lse[:, a:b])
