@@ -1,5 +1,7 @@
 // pfa_bwd.hip -- backward (dQ, dK, dV) of the packed varlen attention forward for gfx950,
 // behind the C ABI (pfa_varlen_bwd).
+#include <type_traits>
+
 #include "pfa_common.h"
 
 namespace {
@@ -19,9 +21,10 @@ namespace {
 //     A operands from transposed LDS reads of the same stages;
 //   * dQ: one work item = 128 queries; the forward's shape: S^T = K Q^T, dP^T = V dO^T
 //     (lanes hold queries), dQ^T += K^T dS^T with K^T from transposed LDS reads.
-// Every stage tile is stored in the K swizzle (row reads conflict-free); the transposed
-// reads take explicit per-lane offsets for each 16-row step and 8-row half, since that
-// swizzle does not keep a constant pattern 8 rows apart.
+// Every stage tile is read both as rows and transposed, so it is stored in the KV swizzle,
+// free of bank conflicts for both patterns; the transposed reads take explicit per-lane
+// offsets for each 16-row step and 8-row half, since the swizzle does not keep a constant
+// pattern 8 rows apart.
 // ---------------------------------------------------------------------------------
 // waves per workgroup (one per SIMD).  dK/dV holds two accumulators and the stationary K
 // and V fragments (419 registers at d = 128), so one workgroup fills a CU; dQ loads its
@@ -83,7 +86,7 @@ __device__ __forceinline__ void t_operands(const char* base, const int (&off)[2]
     }
 }
 
-// Offsets for t_operands over a K-swizzled tile: the same (row, chunk, half) pattern the
+// Offsets for t_operands over a KV-swizzled tile: the same (row, chunk, half) pattern the
 // forward uses for its V^T reads, resolved per row.
 template <int D>
 __device__ __forceinline__ void t_offsets(int lane, int (&off)[2][2][D / 32]) {
@@ -94,7 +97,7 @@ __device__ __forceinline__ void t_offsets(int lane, int (&off)[2][2][D / 32]) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        off[cc][h][dt] = phys_off<D, true>(16 * cc + 8 * h + 4 * g + (i16 >> 2),
+        off[cc][h][dt] = phys_off<D, Swz::KV>(16 * cc + 8 * h + 4 * g + (i16 >> 2),
                                            4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
 }
 
@@ -111,7 +114,7 @@ __device__ __forceinline__ void stage_rows(const f32x16 (&acc)[D / 32], float mu
       bf16x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[dt][4 * ii + e] * mul);
-      *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(n32, 4 * dt + ii) + 8 * g) = w;
+      *reinterpret_cast<bf16x4*>(ost + phys_off<D, Swz::K>(n32, 4 * dt + ii) + 8 * g) = w;
     }
 }
 
@@ -124,7 +127,7 @@ __device__ __forceinline__ void store_rows(const char* ost, int lane, __bf16* ds
     const int P = k * kWave + lane;
     const int r = P / CPR;
     const int ch = P % CPR;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, true>(r, ch));
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, Swz::K>(r, ch));
     if (r < valid) *reinterpret_cast<u32x4*>(dst + (int64_t)r * rs + ch * 8) = x;
   }
 }
@@ -189,7 +192,7 @@ __device__ __forceinline__ bool bwd_item(const BwdParams& p, int u, bool sorted,
 }
 
 // Loads of one 64-row bf16 stage (rows [r0, r0 + 64) of a segment starting at element
-// base, bounded at L) into a K-swizzled LDS tile; rows >= L read as zeros.
+// base, bounded at L) into a KV-swizzled LDS tile; rows >= L read as zeros.
 // TAG keys the instantiation to its kernel (the HIP host pass rejects a specialisation
 // holding buffer-to-LDS load builtins once two kernel templates have used it).
 template <int D, int CPT, int TAG>
@@ -206,6 +209,22 @@ __device__ __forceinline__ void bwd_issue_tile(const __bf16* base, int r0, int L
   for (int i = 0; i < C::CPT; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, src[i], 0, 0, 0);
 }
+
+// Order of a contraction whose 16-deep steps each read two operand fragments from LDS
+// (in consumption order) and issue two MFMAs: the reads run `ahead` steps before the MFMAs
+// that consume them.  With one wave per SIMD nothing else hides the read latency.
+template <int D, int AHEAD>
+__device__ __forceinline__ void pair_read_ahead() {
+  static_assert(AHEAD > 0 && AHEAD < D / 16, "prefetch distance within the contraction");
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+  for (int t = 0; t < D / 16 - AHEAD; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * AHEAD, 0);
+}
+constexpr int kDkdvReadAhead = 3;
 
 // ---- dK / dV
 template <int D>
@@ -238,12 +257,12 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
   const int row_bytes = (int)(rs * 2);
   int koff[C::KSTEP];
 #pragma unroll
-  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
+  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, Swz::KV>(n32, 2 * t + g);
   int toff[2][2][C::DT];
   t_offsets<D>(lane, toff);
   int src[C::CPT];
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) src[i] = logical_src<D, true>((wave * C::CPT + i) * 64 + lane, row_bytes);
+  for (int i = 0; i < C::CPT; ++i) src[i] = logical_src<D, Swz::KV>((wave * C::CPT + i) * 64 + lane, row_bytes);
   if (sorted) __syncthreads();   // s_len aliases the Q ring
 
   for (int u = slot; u < total; u += G) {
@@ -292,8 +311,11 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
     };
     const int ns = (L + kBwdStage - 1) / kBwdStage;
     issue(0, 0);
-    for (int s = 0; s < ns; ++s) {
-      const int cur = s & 1;
+    // One stage; the ring slot is a template constant, so every LDS address is a lane
+    // offset plus an immediate (no per-stage address arithmetic) and the accumulators keep
+    // their registers across the unrolled pair of stages.
+    auto stage = [&](auto slot, int s) {
+      constexpr int cur = decltype(slot)::value;
       __builtin_amdgcn_s_waitcnt(kWaitVmem);
       __syncthreads();
       if (s + 1 < ns) issue(cur ^ 1, s + 1);
@@ -306,10 +328,10 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
         const char* qj = qst + j * 32 * D * 2;
         const char* dj = dst + j * 32 * D * 2;
         f32x16 sc, dp;
+        __builtin_amdgcn_sched_barrier(0);   // the S / dP products form a region of their own
         {
           bf16x8 qa[C::KSTEP], da[C::KSTEP];
-          k_operands<D>(qj, koff, qa);
-          k_operands<D>(dj, koff, da);
+          k_operands2<D>(qj, dj, koff, qa, da);
 #pragma unroll
           for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
 #pragma unroll
@@ -317,7 +339,9 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], kr[t], sc, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], vr[t], dp, 0, 0, 0);
           }
+          pair_read_ahead<D, kDkdvReadAhead>();
         }
+        __builtin_amdgcn_sched_barrier(0);
         // element i holds query row j*32 + 8(i/4) + 4g + i%4 of this key column
         bf16x8 pp[2], dsp[2];
 #pragma unroll
@@ -350,6 +374,10 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
           for (int dt = 0; dt < C::DT; ++dt)
             dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[cc][dt], dsp[cc], dkt[dt], 0, 0, 0);
       }
+    };
+    for (int s = 0; s < ns; s += 2) {   // the ring slot is a constant in each copy
+      stage(std::integral_constant<int, 0>{}, s);
+      if (s + 1 < ns) stage(std::integral_constant<int, 1>{}, s + 1);
     }
     __syncthreads();   // every wave has left the ring
     char* const ok = qring + wave * (32 * D * 2);
@@ -394,12 +422,12 @@ pfa_bwd_dq_kernel(BwdParams p) {
   const int row_bytes = (int)(rs * 2);
   int koff[C::KSTEP];
 #pragma unroll
-  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
+  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, Swz::KV>(n32, 2 * t + g);
   int toff[2][2][C::DT];
   t_offsets<D>(lane, toff);
   int src[C::CPT];
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) src[i] = logical_src<D, true>((wave * C::CPT + i) * 64 + lane, row_bytes);
+  for (int i = 0; i < C::CPT; ++i) src[i] = logical_src<D, Swz::KV>((wave * C::CPT + i) * 64 + lane, row_bytes);
   if (sorted) __syncthreads();   // s_len aliases the K ring
 
   for (int u = slot; u < total; u += G) {
@@ -437,8 +465,8 @@ pfa_bwd_dq_kernel(BwdParams p) {
     const int ns = (L + kBwdStage - 1) / kBwdStage;
     bwd_issue_tile<D, C::CPT, 1>(kbase, 0, L, rs, row_bytes, kring, src, wave);
     bwd_issue_tile<D, C::CPT, 1>(vbase, 0, L, rs, row_bytes, vring, src, wave);
-    for (int s = 0; s < ns; ++s) {
-      const int cur = s & 1;
+    auto stage = [&](auto slot, int s) {
+      constexpr int cur = decltype(slot)::value;
       __builtin_amdgcn_s_waitcnt(kWaitVmem);
       __syncthreads();
       if (s + 1 < ns) {
@@ -496,6 +524,10 @@ pfa_bwd_dq_kernel(BwdParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+    };
+    for (int s = 0; s < ns; s += 2) {   // the ring slot is a constant in each copy
+      stage(std::integral_constant<int, 0>{}, s);
+      if (s + 1 < ns) stage(std::integral_constant<int, 1>{}, s + 1);
     }
     __syncthreads();   // every wave has left the ring
     char* const oq = kring + wave * (32 * D * 2);

@@ -40,29 +40,40 @@ constexpr float kLn2 = 0.6931471805599453f;
 // the 32-bit offsets of a buffer resource.
 constexpr int64_t kMaxRowElems = int64_t(1) << 23;
 
-// LDS layout of a K or V stage: 16-byte chunks, row-major (row = key), with the chunk
-// index XOR-swizzled inside each 256-byte line so the two read patterns are free of bank
-// conflicts: K operand reads (16 lanes = 16 consecutive rows, one logical chunk) and
-// transposed V reads (4 consecutive rows x 64 bytes per 32 lanes).
-__device__ __forceinline__ int swz_k(int line) { return line & 15; }
-__device__ __forceinline__ int swz_v(int line) { return (line & 3) << 2; }
+// LDS layout of a stage tile: 16-byte chunks, row-major, with the chunk index XOR-swizzled
+// inside each 256-byte line (64 banks of 4 bytes) so the read patterns are free of bank
+// conflicts.  Row reads (the K operand: 16 lanes = 16 consecutive rows, one logical chunk)
+// need the swizzle to be a bijection over 16 consecutive rows; transposed reads (4
+// consecutive rows x 64 bytes per 32 lanes) need every aligned group of 4 rows spread
+// over the line's four 64-byte quarters.
+//   K:  row reads only (the forward's K tiles);
+//   V:  transposed reads only (the forward's V tiles);
+//   KV: both (the backward's tiles, read as rows for one product and transposed for
+//       another): the line's two low bit pairs swapped (d = 128: one row per line), or
+//       bit 0 moved above bits 1-2 (d = 64: two rows per line).
+enum class Swz { K, V, KV };
+
+template <int D, Swz SW>
+__device__ __forceinline__ int swz(int line) {
+  if constexpr (SW == Swz::K) return line & 15;
+  if constexpr (SW == Swz::V) return (line & 3) << 2;
+  return D == 128 ? (((line & 3) << 2) | ((line >> 2) & 3)) : (((line & 1) << 2) | ((line >> 1) & 3));
+}
 
 // byte offset of logical (row, chunk) within a stage
-template <int D, bool IS_K>
+template <int D, Swz SW>
 __device__ __forceinline__ int phys_off(int row, int chunk) {
   const int P = row * (D / 8) + chunk;
   const int line = P >> 4;
-  const int sw = IS_K ? swz_k(line) : swz_v(line);
-  return ((line << 4) | ((P & 15) ^ sw)) << 4;
+  return ((line << 4) | ((P & 15) ^ swz<D, SW>(line))) << 4;
 }
 
 // logical byte offset (row * row_bytes + chunk * 16) of the chunk stored at physical
 // chunk position P; the XOR swizzle is its own inverse
-template <int D, bool IS_K>
+template <int D, Swz SW>
 __device__ __forceinline__ int logical_src(int P, int row_bytes) {
   const int line = P >> 4;
-  const int sw = IS_K ? swz_k(line) : swz_v(line);
-  const int Pl = (line << 4) | ((P & 15) ^ sw);
+  const int Pl = (line << 4) | ((P & 15) ^ swz<D, SW>(line));
   return (Pl / (D / 8)) * row_bytes + (Pl % (D / 8)) * 16;
 }
 
@@ -126,6 +137,18 @@ __device__ __forceinline__ void k_operands(const char* kst, const int (&koff)[D 
                                            bf16x8 (&a)[D / 16]) {
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) a[t] = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
+}
+
+// Operand fragments of two 32-row sub-blocks (same lane offsets), read interleaved in the
+// order two MFMA chains that alternate between them consume them: a[0], b[0], a[1], ...
+template <int D>
+__device__ __forceinline__ void k_operands2(const char* ast, const char* bst, const int (&koff)[D / 16],
+                                            bf16x8 (&a)[D / 16], bf16x8 (&b)[D / 16]) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    a[t] = *reinterpret_cast<const bf16x8*>(ast + koff[t]);
+    b[t] = *reinterpret_cast<const bf16x8*>(bst + koff[t]);
+  }
 }
 
 // ---- host side

@@ -184,6 +184,31 @@ __device__ __forceinline__ void qk_mfma(const bf16x8 (&ka)[D / 16], const bf16x8
     }
 }
 
+#ifndef PFA_QK_AHEAD_64
+#define PFA_QK_AHEAD_64 0
+#endif
+#ifndef PFA_QK_AHEAD_128
+#define PFA_QK_AHEAD_128 4
+#endif
+
+// Order of the QK phase of a stage: the two K operand reads of each 16-deep step (one per
+// 32-key sub-block) are issued `ahead` steps before the 2 QB MFMAs that consume them; left
+// to itself the compiler waits on each pair right before its MFMAs.
+template <int D, int QB>
+__device__ __forceinline__ void qk_schedule() {
+  constexpr int ahead = D == 128 ? PFA_QK_AHEAD_128 : PFA_QK_AHEAD_64;
+  static_assert(ahead >= 0 && ahead < D / 16, "prefetch distance within the contraction");
+  if constexpr (ahead > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * ahead, 0);
+#pragma unroll
+    for (int t = 0; t < D / 16 - ahead; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB * ahead, 0);
+  }
+}
+
 // V^T operand fragments of one sub-block: vst points at its first row; voff[dt] is this
 // lane's byte offset for the transposed read of rows 4g + i16/4 at d = 32dt + 16hh +
 // 4(i16 & 3); the second read of each pair is 8 rows further.
@@ -343,6 +368,7 @@ __device__ __forceinline__ void stage_body_fp8(TileState<D, QB>& st, char* __res
   k_operands<D>(kcur, koff, ka);
   k_operands<D>(kcur + 32 * D * 2, koff, kb);
   qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
+  qk_schedule<D, QB>();
   softmax_head64<D, QB>(st, s0, s1, kbase, L, c, g);
   softmax_body8<D, QB>(st, s0, pw, 0, c);
   i32x8 va[D / 32];
@@ -395,6 +421,7 @@ __device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restric
     k_operands<D>(kh, koff, ka);
     k_operands<D>(kh + 32 * D * 2, koff, kb);
     qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
+    qk_schedule<D, QB>();
     softmax_head64<D, QB>(st, s0, s1, key0, L, c, g);
     softmax_body<D, QB>(st, s0, p0, c);
     v_operands<D>(vh, voff, va);
@@ -525,7 +552,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   // ---- per-lane LDS offsets (fixed for the whole tile)
   int koff[C::KSTEP], voff[C::DT];
 #pragma unroll
-  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, true>(n32, 2 * t + g);
+  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, Swz::K>(n32, 2 * t + g);
   if constexpr (mode_fp8(MODE)) {
     // transposed e4m3 reads: lane i16 supplies row i16/2 (keys 4g + 0..3, then 8 + 4g +
     // 0..3) and half i16 & 1 of the 16 channels 32dt + 16hh ..; v8_operand adds 16q rows
@@ -537,7 +564,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   } else {
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
-      voff[dt] = phys_off<D, false>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+      voff[dt] = phys_off<D, Swz::V>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
   }
 
   // ---- stage loads: global -> LDS directly (no registers).  Lane l of the wave's i-th
@@ -553,11 +580,11 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
 #pragma unroll
   for (int i = 0; i < C::CPT; ++i) {
     const int P = (wave * C::CPT + i) * 64 + lane;
-    src_k[i] = logical_src<D, true>(P, kbytes);
+    src_k[i] = logical_src<D, Swz::K>(P, kbytes);
     if constexpr (mode_fp8(MODE)) {
       if (i < C::CPT8) src_v[i] = logical_src8<D>((wave * C::CPT8 + i) * 64 + lane, (int)rs);
     } else {
-      src_v[i] = logical_src<D, false>(P, vbytes);
+      src_v[i] = logical_src<D, Swz::V>(P, vbytes);
     }
   }
   auto issue_fn = [&](char* kdst, char* vdst, int stage) {
@@ -639,7 +666,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
         bf16x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * sc[e]);
-        *reinterpret_cast<bf16x4*>(ost + phys_off<D, true>(r, 4 * dt + ii) + 8 * g) = w;
+        *reinterpret_cast<bf16x4*>(ost + phys_off<D, Swz::K>(r, 4 * dt + ii) + 8 * g) = w;
       }
     const float mfix = mode_fp8(MODE) ? st.m_run[b] - kP8Log2 : st.m_run[b];   // FP8 sums 2^8 p
     if (p.lse != nullptr && g == 0 && q0 + r < Lq)
@@ -653,7 +680,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
     const int P = k * kWave + lane;
     const int r = P / C::CPR;
     const int ch = P % C::CPR;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, true>(r, ch));
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, Swz::K>(r, ch));
     if (q0 + r < Lq)
       *reinterpret_cast<u32x4*>(p.out + (int64_t)(qa + q0 + r) * rs + head_off + ch * 8) = x;
   }
