@@ -503,11 +503,19 @@ pfa_bwd_dq_kernel(BwdParams p) {
         // element i holds key s*64 + j*32 + 8(i/4) + 4g + i%4 for this lane's query
         const int key0 = s * kBwdStage + j * 32;
         bf16x8 dsp[2];
+        if (key0 + 32 <= L) {                       // every key of the sub-block is in the segment
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
-          const float pv = key < L ? __builtin_amdgcn_exp2f(fmaf(sc[i], p.c, nl)) : 0.f;
-          dsp[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl));
+          for (int i = 0; i < 16; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], p.c, nl));
+            dsp[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl));
+          }
+        } else {                                    // the segment's last keys: the rest weigh 0
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
+            const float pv = key < L ? __builtin_amdgcn_exp2f(fmaf(sc[i], p.c, nl)) : 0.f;
+            dsp[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - dl));
+          }
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {             // K^T, one 16-key half at a time
