@@ -27,7 +27,7 @@ namespace {
 // pattern 8 rows apart.
 // ---------------------------------------------------------------------------------
 // waves per workgroup (one per SIMD).  dK/dV holds two accumulators and the stationary K
-// and V fragments (419 registers at d = 128), so one workgroup fills a CU; dQ loads its
+// and V fragments (428 registers at d = 128), so one workgroup fills a CU; dQ loads its
 // two operand sets one after the other and fits 256 registers, so two workgroups share a
 // CU (its few spills are per-item offsets, reloaded outside the stage loop).
 constexpr int kBwdNW = 4;
