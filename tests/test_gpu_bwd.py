@@ -132,3 +132,39 @@ def test_poison_in_other_segments_does_not_leak():
     bad = _run(dataclasses.replace(wl, q=q, k=k, v=v), d2, "poisoned neighbours")
     for g, h in zip(clean, bad):
         np.testing.assert_array_equal(g[a:b], h[a:b])
+
+
+def test_tensors_beyond_two_giga_elements():
+    """Every tensor of 2.26e9 elements (538 segments of 4096 tokens, 8 heads, d 128, built
+    from three seeded blocks, segment s holding block s mod 3): the gradients of the
+    segments just below and above the 2^31-element boundary and of the last segment equal,
+    bitwise, those of the same block run alone (itself checked against the oracle's
+    gradients by the tests above, on smaller shapes)."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_bwd, pfa_varlen_fwd
+    from tests._gpu import to_dev
+    L, H, d, n = 4096, 8, 128, 538
+    T = L * n
+    assert T * H * d > 2 ** 31
+    blocks = [W.make([L], H, d, seed=950 + c, name=f"block{c}") for c in range(3)]
+    douts = [_dout(b, 950 + c) for c, b in enumerate(blocks)]
+    idx = torch.arange(n, device="cuda") % 3
+
+    def tile(arrs):
+        stack = torch.stack([to_dev(a) for a in arrs])
+        return stack[idx].reshape(T, H, d)
+
+    q, k, v = (tile([getattr(b, name) for b in blocks]) for name in ("q", "k", "v"))
+    do = tile(douts)
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    say(f"[gpu] pfa_varlen_bwd beyond 2^31 elements: segs={n} T={T} H={H} d={d}")
+    out, lse = pfa_varlen_fwd(q, k, v, cu, L, blocks[0].scale)
+    dq, dk, dv = pfa_varlen_bwd(q, k, v, out, do, lse, cu, L, blocks[0].scale)
+    torch.cuda.synchronize()
+    alone = [_run(b, douts[c], f"block {c} alone") for c, b in enumerate(blocks)]
+    for s in (511, 512, 537):
+        c = s % 3
+        for g, ref in zip((dq, dk, dv), alone[c]):
+            np.testing.assert_array_equal(from_dev_bf16(g[s * L:(s + 1) * L]), ref)
+    del q, k, v, do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()

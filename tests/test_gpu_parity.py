@@ -199,3 +199,42 @@ def test_running_max_jumps_inside_a_stage(d, scale):
     halves of a 64-key stage), exercising every rescale path of the online softmax."""
     wl = W.make([37, 100, 300, 64, 129], 3, d, seed=81, scale=scale, name="max jumps")
     _full_check(wl, f"max jumps d={d} scale={scale}")
+
+
+def test_tensors_beyond_two_giga_elements():
+    """q, k, v and out of 2.26e9 elements each (above the 32-bit element index range):
+    538 segments of 4096 tokens, 8 heads, d 128, built from three seeded segment blocks
+    (segment s holds block s mod 3, so an index that wrapped at 2^31 elements would land
+    on a segment of another block).  Checked against the oracle on sampled rows of the
+    segments just below and above the 2^31-element boundary and of the last segment, and
+    every sampled segment bitwise against the same block's first segment."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd
+    L, H, d, n = 4096, 8, 128, 538
+    T = L * n
+    assert T * H * d > 2 ** 31
+    blocks = [W.make([L], H, d, seed=900 + c, name=f"block{c}") for c in range(3)]
+    idx = torch.arange(n, device="cuda") % 3
+    big = []
+    for name in ("q", "k", "v"):
+        stack = torch.stack([G.to_dev(getattr(b, name)) for b in blocks])
+        big.append(stack[idx].reshape(T, H, d))
+        del stack
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device="cuda")
+    G.say(f"[gpu] pfa_varlen_fwd beyond 2^31 elements: segs={n} T={T} H={H} d={d}")
+    out, lse = pfa_varlen_fwd(big[0], big[1], big[2], cu, L, blocks[0].scale)
+    torch.cuda.synchronize()
+    rows = W.sample_rows(blocks[0].cu_seqlens, stride=97, edge=16, full_upto=0)
+    refs = {}
+    for c, b in enumerate(blocks):
+        refs[c] = oracle.varlen_fwd(b.q, b.k, b.v, b.cu_seqlens, b.scale, rows=rows)
+    first = {c: G.from_dev_bf16(out[c * L:(c + 1) * L]) for c in range(3)}
+    for s in (511, 512, 537):          # 512 * 4096 * 8 * 128 = 2^31 elements
+        c = s % 3
+        ob = G.from_dev_bf16(out[s * L:(s + 1) * L])
+        ls = lse[:, s * L:(s + 1) * L].cpu().numpy()
+        np.testing.assert_array_equal(ob, first[c])
+        o_ref, l_ref = refs[c]
+        G.assert_parity(G.compare(ob[rows], ls[:, rows], o_ref, l_ref), f"segment {s} (block {c})")
+    del big, out, lse
+    torch.cuda.empty_cache()
