@@ -80,6 +80,17 @@ def calibrate_copy():
                       "bytes_written_per_copy": n, "copies": 3}))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, out_bits, lse, budget_s: float):
     """Time the fp64 oracle on a bounded row sample of the same workload and compare the
     GPU output on those rows."""
@@ -108,7 +119,7 @@ def cpu_baseline(wl, out_bits, lse, budget_s: float):
               "rel_rms": float(np.sqrt((diff * diff).sum() / (o_ref * o_ref).sum())),
               "lse_max_abs_err": float(np.abs(lse[:, rows].astype(np.float64) - l_ref).max())}
     base = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} uniformly drawn query rows of {wl.name} (all heads, each row against "
                       f"its whole segment), {flop / 1e9:.1f} GFLOP of fp64 work in {dt:.1f} s"}
     return base, parity
@@ -134,6 +145,22 @@ def timed(step, stream, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall * 1e3 / steps, ev0.elapsed_time(ev1) / steps
+
+
+def launch_stats(step, stream, n):
+    """After the timed region: n more launches, each between its own pair of HIP events on
+    the launch stream; median and minimum of the per-launch durations."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"launches": n, "median_ms": round(ms[n // 2] if n % 2 else 0.5 * (ms[n // 2 - 1] + ms[n // 2]), 5),
+            "min_ms": round(ms[0], 5)}
 
 
 def bench_cross(args):
@@ -759,6 +786,8 @@ def main():
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (kernel_ms * 1e-3) / 1e12
     traffic = measured_traffic(args.config)
+    launches = launch_stats(step, stream, 10 if flop > 1e13 else 50)
+    alg_bytes = wl.total_tokens * wl.heads * (8 * wl.head_dim + 4)
 
     out_bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
     lse_h = lse.cpu().numpy()
@@ -798,7 +827,10 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_ms": round(kernel_ms, 5),
+            "algorithmic_bytes": alg_bytes,
+            "algorithmic_gbs": round(alg_bytes / (kernel_ms * 1e-3) / 1e9, 1),
         },
+        "launch_stats": launches,
         "cpu_baseline": cpu,
         "parity_on_sample": parity,
     }
