@@ -310,3 +310,70 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+# ---- property tests of the host validators (hypothesis), against their definitions
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=300, deadline=None)
+@given(cu=st.lists(st.integers(-5, 300), min_size=2, max_size=20), mx=st.integers(1, 100))
+def test_cu_seqlens_validator_matches_its_definition(lib, cu, mx):
+    from packed_varlen_flash_amd import PfaError, pfa_check_cu_seqlens
+    d = np.diff(cu)
+    valid = cu[0] == 0 and bool(np.all(d >= 0)) and bool(np.all(d <= mx))
+    if valid:
+        assert pfa_check_cu_seqlens(cu, mx) == cu[-1]
+    else:
+        with pytest.raises(PfaError) as e:
+            pfa_check_cu_seqlens(cu, mx)
+        assert e.value.status == -8
+
+
+@st.composite
+def _sparse_layouts(draw):
+    heads = draw(st.integers(1, 3))
+    lh = draw(st.sampled_from(sorted({1, heads})))
+    lengths = draw(st.lists(st.integers(0, 700), min_size=1, max_size=4))
+    layout = []
+    for _ in range(lh):
+        segs = []
+        for L in lengths:
+            nkb = -(-L // 64)
+            rows = []
+            for _ in range(-(-L // 256)):
+                rows.append(draw(st.lists(st.integers(0, nkb - 1), min_size=1, max_size=nkb, unique=True)))
+            segs.append(rows)
+        layout.append(segs)
+    return heads, lengths, layout
+
+
+@settings(max_examples=150, deadline=None)
+@given(case=_sparse_layouts(), mutation=st.integers(0, 3), pick=st.integers(0, 10 ** 6))
+def test_block_layout_validator_matches_its_definition(lib, case, mutation, pick):
+    """Well-formed layouts (every existing query block lists distinct, in-range key blocks)
+    are accepted; a duplicated entry, an out-of-range entry or an emptied query block is
+    rejected."""
+    from packed_varlen_flash_amd import PfaError, block_layout_csr, pfa_check_block_layout
+    heads, lengths, layout = case
+    mx = max(max(lengths), 1)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rows = [(hl, s, qb) for hl in range(len(layout)) for s in range(len(lengths))
+            for qb in range(len(layout[hl][s]))]
+    if mutation and rows:
+        hl, s, qb = rows[pick % len(rows)]
+        row = layout[hl][s][qb]
+        if mutation == 1:
+            row.append(row[0])                     # listed twice
+        elif mutation == 2:
+            row.append(-(-lengths[s] // 64))       # one block past the segment's last
+        else:
+            row.clear()                            # a query block with no keys
+    kv_ptr, kv_idx, lh = block_layout_csr(layout, lengths, mx)
+    if mutation and rows:
+        with pytest.raises(PfaError) as e:
+            pfa_check_block_layout(cu, mx, heads, lh, kv_ptr, kv_idx)
+        assert e.value.status == -13
+    else:
+        pfa_check_block_layout(cu, mx, heads, lh, kv_ptr, kv_idx)
