@@ -69,7 +69,9 @@ def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
     q, k, v: bf16 CUDA tensors [T, H, d] (d = 64 or 128), contiguous.
     cu_seqlens: int32 CUDA tensor [num_seqs + 1].  max_seqlen: bound on segment lengths.
     Returns (out [T, H, d] bf16, lse [H, T] fp32 or None), enqueued on ``stream``
-    (default: PyTorch's current stream).
+    (default: PyTorch's current stream).  T must equal cu_seqlens[-1]: the library takes T
+    from the table on the device (it lays LSE out with that row stride), and this binding
+    does not read the table on the host; pfa_check_cu_seqlens checks a host copy.
     """
     import torch
 
