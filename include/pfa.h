@@ -149,7 +149,7 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v,
  * k_rot       with tables: device bf16 [T, heads, head_dim] workspace, 16-byte aligned,
  *             owned by the caller; on return (stream-ordered) it holds the rotated keys.
  *             Keys are rotated there by one pass before the attention kernel, which
- *             re-reads every key once per 128-query tile; queries are rotated in
+ *             re-reads every key once per 256-query tile; queries are rotated in
  *             registers as they are loaded.  Ignored (may be NULL) without tables.
  * out, lse    as for pfa_varlen_fwd (out 16-byte aligned).
  * cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale, stream: as for pfa_varlen_fwd.
