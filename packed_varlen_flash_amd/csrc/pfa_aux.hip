@@ -70,8 +70,11 @@ __global__ void __launch_bounds__(kMergeThreads) pfa_merge_kernel(MergeParams m)
 // codes, and finally the scales over the maxima.  All HBM-bound.
 // ---------------------------------------------------------------------------------
 constexpr int kQuantThreads = 256;
-constexpr int kQuantTokens = 64;   // tokens per thread in the maxima pass
 constexpr int kQuantUnroll = 8;    // loads in flight per thread; tokens per thread in the codes pass
+constexpr int kAmaxBlock = 512;    // tokens per work unit of the maxima pass
+constexpr int kAmaxWaves = 8;      // waves per maxima workgroup
+constexpr int kAmaxThreads = 64 * kAmaxWaves;
+static_assert(kAmaxThreads == 64 * 8, "the LDS reduction gives each thread one (chunk, element) pair");
 
 struct QuantParams {
   const __bf16* v;
@@ -108,42 +111,67 @@ __global__ void __launch_bounds__(kQuantThreads) pfa_v8_zero_kernel(QuantParams 
     reinterpret_cast<uint32_t*>(q.v_scale)[i] = 0u;
 }
 
-__global__ void __launch_bounds__(kQuantThreads) pfa_v8_amax_kernel(QuantParams q) {
+// Maxima over one work unit: a kAmaxBlock-token block of the packed rows times a group of
+// 64 chunk columns (16 bytes each).  Lane l owns chunk column 64 g + l; wave w reads the
+// block's tokens w, w + kAmaxWaves, ..., so each load instruction covers 1 KB of one row.
+// Per segment run of the block the waves' maxima meet in LDS, and one atomic per
+// (segment, channel) leaves the workgroup: the same-address atomics of a long segment are
+// what bound this pass when every thread issued its own.
+__global__ void __launch_bounds__(kAmaxThreads) pfa_v8_amax_kernel(QuantParams q) {
+  __shared__ float part[kAmaxWaves][8][64];
   const int64_t T = q.cu[q.num_seqs];
   const int cpt = q.heads * q.d / 8;                      // 16-byte chunks per token
-  const int64_t items = (T > 0 ? (T + kQuantTokens - 1) / kQuantTokens : 0) * cpt;
-  for (int64_t it = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; it < items;
-       it += (int64_t)gridDim.x * kQuantThreads) {
-    const int64_t t0 = it / cpt * kQuantTokens;
-    const int j = (int)(it % cpt);
-    const int64_t t1 = t0 + kQuantTokens < T ? t0 + kQuantTokens : T;
+  const int ncg = (cpt + 63) / 64;
+  const int64_t units = (T + kAmaxBlock - 1) / kAmaxBlock * ncg;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {   // uniform over the workgroup
+    const int64_t t0 = u / ncg * kAmaxBlock;
+    const int jg = (int)(u % ncg) * 64;
+    const int j = jg + lane;
+    const int64_t t1 = t0 + kAmaxBlock < T ? t0 + kAmaxBlock : T;
     const __bf16* src = q.v + 8 * j;
     int seg = segment_of(q.cu, q.num_seqs, t0);
-    int64_t t = t0;
-    while (t < t1) {
-      // the run of tokens of this item inside segment seg
+    int64_t rs = t0;
+    while (rs < t1) {                                       // one segment run per pass
       const int64_t seg_end = q.cu[seg + 1];
-      const int64_t run_end = seg_end < t1 ? seg_end : t1;
+      const int64_t re = seg_end < t1 ? seg_end : t1;
       float mx[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (; t + kQuantUnroll <= run_end; t += kQuantUnroll) {   // independent loads in flight
-        bf16x8 x[kQuantUnroll];
+      if (j < cpt) {
+        // this wave's first token at or after the run start
+        int64_t t = t0 + w;
+        if (rs - t0 > w) t += (rs - t0 - w + kAmaxWaves - 1) / kAmaxWaves * kAmaxWaves;
+        for (; t + (int64_t)(kQuantUnroll - 1) * kAmaxWaves < re; t += (int64_t)kQuantUnroll * kAmaxWaves) {
+          bf16x8 x[kQuantUnroll];
 #pragma unroll
-        for (int u = 0; u < kQuantUnroll; ++u) x[u] = *reinterpret_cast<const bf16x8*>(src + (t + u) * cpt * 8);
+          for (int i = 0; i < kQuantUnroll; ++i)
+            x[i] = *reinterpret_cast<const bf16x8*>(src + (t + (int64_t)i * kAmaxWaves) * cpt * 8);
 #pragma unroll
-        for (int u = 0; u < kQuantUnroll; ++u)
+          for (int i = 0; i < kQuantUnroll; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[u][e]));
+            for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[i][e]));
+        }
+        for (; t < re; t += kAmaxWaves) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + t * cpt * 8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[e]));
+        }
       }
-      for (; t < run_end; ++t) {
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + t * cpt * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx[e] = fmaxf(mx[e], fabsf((float)x[e]));
+      for (int e = 0; e < 8; ++e) part[w][e][lane] = mx[e];
+      __syncthreads();
+      {
+        const int c = threadIdx.x & 63, e = threadIdx.x >> 6;   // one (chunk, element) per thread
+        float m = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kAmaxWaves; ++ww) m = fmaxf(m, part[ww][e][c]);
+        if (jg + c < cpt && m > 0.f)
+          atomicMax(reinterpret_cast<uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * (jg + c) + e,
+                    __float_as_uint(m));
       }
-      uint32_t* dst = reinterpret_cast<uint32_t*>(q.v_scale) + ((int64_t)seg * q.heads) * q.d + 8 * j;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (mx[e] > 0.f) atomicMax(dst + e, __float_as_uint(mx[e]));
-      while (t < t1 && q.cu[seg + 1] <= t) ++seg;    // next non-empty segment
+      __syncthreads();
+      rs = re;
+      while (rs < t1 && q.cu[seg + 1] <= rs) ++seg;         // next non-empty segment
     }
   }
 }
@@ -233,9 +261,10 @@ PFA_API int pfa_quantize_v_fp8(const void* v, const int32_t* cu_seqlens, int num
                         reinterpret_cast<const void*>(&pfa_v8_amax_kernel),
                         reinterpret_cast<const void*>(&pfa_v8_codes_kernel),
                         reinterpret_cast<const void*>(&pfa_v8_scale_kernel)};
-  const unsigned grids[4] = {(unsigned)cus, (unsigned)cus * 8, (unsigned)cus * 8, (unsigned)cus};
+  const unsigned grids[4] = {(unsigned)cus, (unsigned)cus * 4, (unsigned)cus * 8, (unsigned)cus};
+  const unsigned threads[4] = {kQuantThreads, kAmaxThreads, kQuantThreads, kQuantThreads};
   for (int i = 0; i < 4; ++i)
-    if (hipLaunchKernel(fns[i], dim3(grids[i]), dim3(kQuantThreads), args, 0, stream) != hipSuccess)
+    if (hipLaunchKernel(fns[i], dim3(grids[i]), dim3(threads[i]), args, 0, stream) != hipSuccess)
       return PFA_ERR_LAUNCH;
   return PFA_OK;
 }
