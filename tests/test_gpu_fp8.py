@@ -2,6 +2,8 @@
 against the oracle's, and the forward (pfa_varlen_fwd_fp8pv) against (a) exact attention on
 the dequantised V within the per-element bound of the FP8 weights, and (b) the oracle's
 emulation of the blocked FP8 steps, through the C ABI."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -131,3 +133,25 @@ def test_many_segments_unsorted_schedule():
     lengths = [int(x) for x in rng.integers(0, 200, size=650)]
     wl = W.make(lengths, 2, 64, seed=413, name="650 segments")
     _run(wl, "650 segments, unsorted schedule")
+
+
+@pytest.mark.parametrize("heads,d", [(5, 128), (13, 64), (1, 64), (24, 128)])
+def test_quantiser_block_runs_and_partial_chunk_groups_bitwise(heads, d):
+    # the maxima pass works on 512-token blocks x 64 chunk columns of 16 bytes: head counts
+    # whose rows end inside a chunk group, segments that start and end inside a block,
+    # several segments in one block, and large values (either sign) planted in late blocks
+    # of a long segment, so a maximum from any block must reach its segment's scale
+    lengths = [3000, 1, 0, 511, 513, 37, 1024, 2]
+    wl = W.make(lengths, heads, d, seed=420 + heads, name=f"quantiser runs H={heads} d={d}")
+    v = wl.v.copy()
+    rng = np.random.default_rng(421 + heads)
+    for t in (2999, 2100, 1537, 600):
+        h, c = int(rng.integers(0, heads)), int(rng.integers(0, d))
+        v[t, h, c] = 0x4480 if t % 2 else 0xC480            # +-1024 in bf16
+    v[3000 + 511 + 500, 0, d - 1] = 0xC480                    # inside the 513-token segment
+    w2 = dataclasses.replace(wl, v=v)
+    v8, vs, _ = _quantize(w2, f"H={heads} d={d}")
+    codes, scales = oracle.quantize_v_fp8(w2.v, w2.cu_seqlens)
+    np.testing.assert_array_equal(v8.cpu().numpy(), codes)
+    np.testing.assert_array_equal(vs.cpu().numpy().astype(np.float64), scales)
+    assert scales.max() >= 1024 / 448                          # the planted values set scales
