@@ -9,6 +9,7 @@ device memory and streams, nothing else.
 from __future__ import annotations
 
 import ctypes
+import itertools
 
 import numpy as np
 
@@ -58,8 +59,26 @@ def _check_table(name, cu, torch):
         raise ValueError(f"{name} must be a contiguous 1-D int32 CUDA tensor")
 
 
+_PLACEHOLDER_SLOTS = 64
+_placeholders = {}
+_next_slot = itertools.count()
+
+
 def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    """Device address of t for the C ABI.  A tensor with no elements has no storage, and
+    the library rejects NULL; such a tensor gets a distinct 256-byte slot of a small
+    per-device buffer instead.  The library reads and writes no rows there: a pack whose
+    table holds no tokens (or no keys) gives the kernels no work on those buffers."""
+    if t is None:
+        return None
+    if t.numel() > 0:
+        return ctypes.c_void_p(t.data_ptr())
+    import torch
+    buf = _placeholders.get(t.device)
+    if buf is None:
+        buf = _placeholders[t.device] = torch.zeros(_PLACEHOLDER_SLOTS * 256, dtype=torch.uint8,
+                                                    device=t.device)
+    return ctypes.c_void_p(buf.data_ptr() + 256 * (next(_next_slot) % _PLACEHOLDER_SLOTS))
 
 
 def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None,
@@ -96,10 +115,8 @@ def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-        ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, int(max_seqlen), H, d,
-        float(scale), ctypes.c_void_p(out.data_ptr()),
-        ctypes.c_void_p(lse.data_ptr()) if lse is not None else None,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), H, d,
+        float(scale), _ptr(out), _ptr(lse),
         ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise PfaError(rc)
