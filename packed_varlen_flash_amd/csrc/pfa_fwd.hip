@@ -45,7 +45,10 @@ namespace {
 // exactly 1 and carries no bf16 rounding; a positive slack saves rescales (about 5% on
 // 4096-token segments) but leaves that weight rounded, which on sharp softmax rows pushes
 // the worst output error past 1e-2 of the exact result.
-constexpr float kRescaleSlack = 0.0f;
+#ifndef PFA_RESCALE_SLACK
+#define PFA_RESCALE_SLACK 0.0f
+#endif
+constexpr float kRescaleSlack = PFA_RESCALE_SLACK;
 
 struct Params {
   const __bf16* q;
@@ -96,6 +99,10 @@ __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kSparseMaxBlocks = 1024;
 constexpr int kSparseLdsBytes = (kSparseMaxBlocks + 4) * 4;
 
+#ifndef PFA_LOAD_ALL
+#define PFA_LOAD_ALL 1
+#endif
+
 // Workgroup geometry at both head sizes: 8 wave64s, wave w owns query rows 32w .. 32w+31 of
 // a 256-row tile.  The hardware places wave w on SIMD w % 4, so waves 0-3 (group 0) and
 // 4-7 (group 1) put one wave of each group on every SIMD.  Keys come in 64-key stages.
@@ -110,6 +117,11 @@ struct Tile {
   static constexpr int NCH = SK * CPR;              // 16-byte chunks of one stage
   static constexpr int CPT = NCH / THREADS;         // ... per thread
   static constexpr int NCH8 = SK * D / 16;          // 16-byte chunks of one e4m3 V stage
+  // Stage loads are issued by the waves of one group (the one in its softmax step at
+  // the even slots where loads go out), or by all waves with PFA_LOAD_ALL.
+  static constexpr int LW = PFA_LOAD_ALL ? NW : NW / 2;   // loading waves
+  static constexpr int CPL = NCH / (LW * kWave);           // bf16 chunks per loading lane
+  static constexpr int CPL8 = NCH8 >= LW * kWave ? NCH8 / (LW * kWave) : 1;   // e4m3 chunks
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
@@ -305,7 +317,7 @@ __device__ __forceinline__ void mfma_step8(TileState<D>& st, f32x16& s0, f32x16&
 // wave's MFMAs that accumulate into it ran in its previous slot.
 template <int D>
 __device__ __forceinline__ void softmax_head64(TileState<D>& st, f32x16& s0, f32x16& s1, int key0, int L,
-                                               float c, int g) {
+                                               float c, int g, float slack) {
   if (key0 + 64 > L) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -321,7 +333,7 @@ __device__ __forceinline__ void softmax_head64(TileState<D>& st, f32x16& s0, f32
   for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
   mx = partner_max(mx);
   const float mb = mx * c;
-  if (__builtin_amdgcn_ballot_w64(mb > st.m_run + kRescaleSlack) != 0) {
+  if (__builtin_amdgcn_ballot_w64(mb > st.m_run + slack) != 0) {
     const float m_new = fmaxf(st.m_run, mb);
     const float a = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
@@ -533,50 +545,56 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
   // within int range.
   const int kbytes = (int)(k_rs * 2);
   const int vbytes = (int)(v_rs * 2);
-  int src_k[C::CPT], src_v[C::CPT];      // logical source offsets of this lane's chunks
+  const bool loader = PFA_LOAD_ALL || grp == 1;
+  const int lw = PFA_LOAD_ALL ? wave : wave - C::NW / 2;   // index among the loading waves
+  int src_k[C::CPL], src_v[C::CPL];      // logical source offsets of this lane's chunks
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int P = (wave * C::CPT + i) * 64 + lane;
+  for (int i = 0; i < C::CPL; ++i) {
+    const int P = (lw * C::CPL + i) * 64 + lane;
     src_k[i] = logical_src<D, Swz::K>(P, kbytes);
     if constexpr (mode_fp8(MODE)) {
-      if (i == 0) src_v[i] = logical_src8<D>(wave * 64 + lane, (int)rs);
+      if (i < C::CPL8) src_v[i] = logical_src8<D>((lw * C::CPL8 + i) * 64 + lane, (int)rs);
     } else {
       src_v[i] = logical_src<D, Swz::V>(P, vbytes);
     }
   }
   auto issue_k = [&](int stage) {
+    if (!loader) return;
     const int kb = stage_key(stage);
     const int rows = (Lk - kb < C::SK) ? (Lk - kb) : C::SK;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * k_rs), 0, rows * kbytes, kRsrcFlags);
-    char* kdst = kring + (stage & 1) * C::TILE_BYTES + wave * C::CPT * 1024;
+    char* kdst = kring + (stage & 1) * C::TILE_BYTES + lw * C::CPL * 1024;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i)
+    for (int i = 0; i < C::CPL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16, src_k[i], 0, 0, 0);
   };
   auto issue_v = [&](int stage) {
+    if (!loader) return;
     const int kb = stage_key(stage);
     const int rows = (Lk - kb < C::SK) ? (Lk - kb) : C::SK;
     if constexpr (mode_fp8(MODE)) {
-      if (wave < C::NCH8 / kWave) {
+      if (lw * C::CPL8 * kWave < C::NCH8) {
         __amdgpu_buffer_rsrc_t r8 = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(v8base + (int64_t)kb * rs), 0, rows * (int)rs, kRsrcFlags);
-        char* vdst = vring + (stage & 1) * C::TILE_BYTES + wave * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)vdst, 16, src_v[0], 0, 0, 0);
+        char* vdst = vring + (stage & 1) * C::TILE_BYTES + lw * C::CPL8 * 1024;
+#pragma unroll
+        for (int i = 0; i < C::CPL8; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
       }
     } else {
       __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * v_rs), 0, rows * vbytes, kRsrcFlags);
-      char* vdst = vring + (stage & 1) * C::TILE_BYTES + wave * C::CPT * 1024;
+      char* vdst = vring + (stage & 1) * C::TILE_BYTES + lw * C::CPL * 1024;
 #pragma unroll
-      for (int i = 0; i < C::CPT; ++i)
+      for (int i = 0; i < C::CPL; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
     }
   };
   // Start of slot t: at even slots the loads issued two slots earlier must have landed
   // (each wave waits for its own, the barrier for everyone's); then the next go out.
   auto slot = [&](int t) {
-    if ((t & 1) == 0 && t > 0) __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    if ((t & 1) == 0 && t > 0 && loader) __builtin_amdgcn_s_waitcnt(kWaitVmem);
     slot_barrier();
     if ((t & 1) == 0) {
       const int u = t >> 1;
@@ -593,7 +611,8 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
     for (int dt = 0; dt < C::DT; ++dt) pin(st.o[dt]);
   };
   auto softmax_step = [&](int j) {
-    softmax_head64<D>(st, s0, s1, stage_key(j), Lk, c, g);
+    // FP8 weights must stay below 448: no slack there
+    softmax_head64<D>(st, s0, s1, stage_key(j), Lk, c, g, mode_fp8(MODE) ? 0.f : kRescaleSlack);
     if constexpr (mode_fp8(MODE)) {
       softmax_body8<D>(st, s0, pw, 0, c);
       softmax_body8<D>(st, s1, pw, 1, c);
@@ -639,7 +658,7 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
 
   if (ns > 0) {
     issue_k(0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    if (loader) __builtin_amdgcn_s_waitcnt(kWaitVmem);
     if (grp == 1) slot(0);
     // QK of stage 0 (K slot 0): S_0
     slot(grp);
