@@ -113,7 +113,10 @@ def cpu_baseline(wl, out_bits, lse, budget_s: float):
     o = W.bf16_to_f64(out_bits[rows])
     diff = np.abs(o - o_ref)
     small = np.abs(o_ref) < 4.0      # where bf16 output rounding stays within 2^-7
-    parity = {"rows": int(n), "max_abs_err": float(diff.max()),
+    # raw max|err| against the 1e-2 bar as written, and how many sampled elements exceed
+    # it (those pass only where |O_ref| >= 4, where bf16 output rounding alone can)
+    parity = {"rows": int(n), "max_abs_err": float(diff.max()), "raw_bar": 1e-2,
+              "n_over_raw_bar": int(np.count_nonzero(diff > 1e-2)),
               "max_abs_err_ref_below_4": float(diff[small].max()) if small.any() else 0.0,
               "n_ref_at_least_4": int((~small).sum()),
               "rel_rms": float(np.sqrt((diff * diff).sum() / (o_ref * o_ref).sum())),

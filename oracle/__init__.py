@@ -49,22 +49,33 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pfa_oracle.c")
-_SO = os.path.join(_HERE, "liboracle.so")
+# PFA_ORACLE_LIB selects another build of the same source (the sanitizer leg of the CPU
+# tests loads an address/undefined-behaviour sanitized copy this way)
+_SO = os.environ.get("PFA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 ELEM_F64 = 0
 ELEM_BF16 = 1
 
 
-def build(force: bool = True) -> str:
-    """Compile ``liboracle.so`` with gcc (fp64, OpenMP, no FMA contraction)."""
-    if force or not os.path.exists(_SO):
-        tmp = _SO + ".tmp"
+def build(force: bool = True, sanitize: bool = False, path: str | None = None) -> str:
+    """Compile ``liboracle.so`` with gcc (fp64, OpenMP, no FMA contraction).
+
+    sanitize: build with AddressSanitizer and UndefinedBehaviorSanitizer (any report
+    aborts), for the CPU tests' sanitizer leg; the process must preload gcc's libasan.
+    path: where to write the library (default: next to this file)."""
+    out = path or _SO
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-               "-std=c11", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-std=c11", "-Wall", "-Wextra"]
+        if sanitize:
+            cmd += ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all"]
+        cmd += ["-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _SO)
-    return _SO
+        os.replace(tmp, out)
+    return out
 
 
 def _load():

@@ -59,6 +59,20 @@ def _check_table(name, cu, torch):
         raise ValueError(f"{name} must be a contiguous 1-D int32 CUDA tensor")
 
 
+def _check_buffer(name, t, device, dtype, shape):
+    """A tensor the caller passes for the library to read or write: it must live on
+    ``device`` (the first input's), have exactly ``dtype`` and ``shape`` and be contiguous,
+    since the library receives only its address."""
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 _PLACEHOLDER_SLOTS = 64
 _placeholders = {}
 _next_slot = itertools.count()
@@ -101,17 +115,20 @@ def pfa_varlen_fwd(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
         raise ValueError("q, k and v must have the same shape")
     if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous():
         raise ValueError("cu_seqlens must be a contiguous int32 CUDA tensor")
+    for name, t in (("k", k), ("v", v), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     T, H, d = q.shape
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    else:
+        _check_buffer("out", out, q.device, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd(
@@ -139,17 +156,20 @@ def pfa_varlen_fwd_qk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, ma
     _check_table("cu_seqlens_k", cu_seqlens_k, torch)
     if cu_seqlens_q.numel() != cu_seqlens_k.numel():
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    for name, t in (("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     Tq, H, d = q.shape
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    else:
+        _check_buffer("out", out, q.device, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (H, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, Tq]")
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (H, Tq))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd_qk(
@@ -178,32 +198,30 @@ def pfa_varlen_fwd_qkv(qkv, cu_seqlens, max_seqlen: int, scale: float | None = N
             or qkv.shape[1] != 3):
         raise ValueError("qkv must be a contiguous bf16 CUDA tensor [T, 3, H, d]")
     _check_table("cu_seqlens", cu_seqlens, torch)
+    if cu_seqlens.device != qkv.device:
+        raise ValueError(f"cu_seqlens must be on {qkv.device}")
     T, _, H, d = qkv.shape
     if (rope_cos is None) != (rope_sin is None):
         raise ValueError("pass both rope_cos and rope_sin, or neither")
     if rope_cos is not None:
         for name, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
-            if (not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
-                    or tuple(t.shape) != (T, d // 2)):
-                raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor [T, d/2]")
+            _check_buffer(name, t, qkv.device, torch.float32, (T, d // 2))
         if k_rot is None:
             k_rot = torch.empty((T, H, d), dtype=torch.bfloat16, device=qkv.device)
         else:
-            _check_bf16("k_rot", k_rot, torch)
-            if tuple(k_rot.shape) != (T, H, d):
-                raise ValueError("k_rot must be [T, H, d]")
+            _check_buffer("k_rot", k_rot, qkv.device, torch.bfloat16, (T, H, d))
     else:
         k_rot = None
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty((T, H, d), dtype=torch.bfloat16, device=qkv.device)
-    elif tuple(out.shape) != (T, H, d) or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor [T, H, d]")
+    else:
+        _check_buffer("out", out, qkv.device, torch.bfloat16, (T, H, d))
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=qkv.device)
-    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    elif lse is not None:
+        _check_buffer("lse", lse, qkv.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device)
     rc = _lib.load().pfa_varlen_fwd_qkv(
@@ -278,6 +296,9 @@ def pfa_varlen_fwd_blocksparse(q, k, v, cu_seqlens, max_seqlen: int, kv_ptr, kv_
     _check_table("kv_ptr", kv_ptr, torch)
     if kv_idx.numel() > 0:
         _check_table("kv_idx", kv_idx, torch)
+    for name, t in (("k", k), ("v", v), ("cu_seqlens", cu_seqlens), ("kv_ptr", kv_ptr), ("kv_idx", kv_idx)):
+        if t.numel() > 0 and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     T, H, d = q.shape
     rows = (cu_seqlens.numel() - 1) * int(layout_heads) * (-(-int(max_seqlen) // SPARSE_BLOCK_Q))
     if kv_ptr.numel() != rows + 1:
@@ -286,12 +307,12 @@ def pfa_varlen_fwd_blocksparse(q, k, v, cu_seqlens, max_seqlen: int, kv_ptr, kv_
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    else:
+        _check_buffer("out", out, q.device, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd_blocksparse(
@@ -311,16 +332,18 @@ def pfa_quantize_v_fp8(v, cu_seqlens, v8=None, v_scale=None, stream=None):
 
     _check_bf16("v", v, torch)
     _check_table("cu_seqlens", cu_seqlens, torch)
+    if cu_seqlens.device != v.device:
+        raise ValueError(f"cu_seqlens must be on {v.device}")
     T, H, d = v.shape
     n = cu_seqlens.numel() - 1
     if v8 is None:
         v8 = torch.empty((T, H, d), dtype=torch.uint8, device=v.device)
-    elif v8.dtype != torch.uint8 or tuple(v8.shape) != (T, H, d) or not v8.is_contiguous():
-        raise ValueError("v8 must be a contiguous uint8 tensor [T, H, d]")
+    else:
+        _check_buffer("v8", v8, v.device, torch.uint8, (T, H, d))
     if v_scale is None:
         v_scale = torch.empty((n, H, d), dtype=torch.float32, device=v.device)
-    elif v_scale.dtype != torch.float32 or tuple(v_scale.shape) != (n, H, d) or not v_scale.is_contiguous():
-        raise ValueError("v_scale must be a contiguous fp32 tensor [num_seqs, H, d]")
+    else:
+        _check_buffer("v_scale", v_scale, v.device, torch.float32, (n, H, d))
     if stream is None:
         stream = torch.cuda.current_stream(v.device)
     rc = _lib.load().pfa_quantize_v_fp8(_ptr(v), _ptr(cu_seqlens), n, H, d, _ptr(v8), _ptr(v_scale),
@@ -343,21 +366,21 @@ def pfa_varlen_fwd_fp8pv(q, k, v8, v_scale, cu_seqlens, max_seqlen: int, scale: 
     _check_table("cu_seqlens", cu_seqlens, torch)
     T, H, d = q.shape
     n = cu_seqlens.numel() - 1
-    if v8.dtype != torch.uint8 or tuple(v8.shape) != (T, H, d) or not v8.is_contiguous() or not v8.is_cuda:
-        raise ValueError("v8 must be a contiguous uint8 CUDA tensor [T, H, d]")
-    if (v_scale.dtype != torch.float32 or tuple(v_scale.shape) != (n, H, d) or not v_scale.is_contiguous()
-            or not v_scale.is_cuda):
-        raise ValueError("v_scale must be a contiguous fp32 CUDA tensor [num_seqs, H, d]")
+    for name, t in (("k", k), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    _check_buffer("v8", v8, q.device, torch.uint8, (T, H, d))
+    _check_buffer("v_scale", v_scale, q.device, torch.float32, (n, H, d))
     if scale is None:
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    else:
+        _check_buffer("out", out, q.device, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd_fp8pv(
@@ -385,11 +408,11 @@ def pfa_varlen_fwd_blocksparse_fp8pv(q, k, v8, v_scale, cu_seqlens, max_seqlen: 
         _check_table("kv_idx", kv_idx, torch)
     T, H, d = q.shape
     n = cu_seqlens.numel() - 1
-    if v8.dtype != torch.uint8 or tuple(v8.shape) != (T, H, d) or not v8.is_contiguous() or not v8.is_cuda:
-        raise ValueError("v8 must be a contiguous uint8 CUDA tensor [T, H, d]")
-    if (v_scale.dtype != torch.float32 or tuple(v_scale.shape) != (n, H, d) or not v_scale.is_contiguous()
-            or not v_scale.is_cuda):
-        raise ValueError("v_scale must be a contiguous fp32 CUDA tensor [num_seqs, H, d]")
+    for name, t in (("k", k), ("cu_seqlens", cu_seqlens), ("kv_ptr", kv_ptr), ("kv_idx", kv_idx)):
+        if t.numel() > 0 and t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    _check_buffer("v8", v8, q.device, torch.uint8, (T, H, d))
+    _check_buffer("v_scale", v_scale, q.device, torch.float32, (n, H, d))
     rows = n * int(layout_heads) * (-(-int(max_seqlen) // SPARSE_BLOCK_Q))
     if kv_ptr.numel() != rows + 1:
         raise ValueError(f"kv_ptr must have {rows + 1} entries for this max_seqlen and layout_heads")
@@ -397,12 +420,12 @@ def pfa_varlen_fwd_blocksparse_fp8pv(q, k, v8, v_scale, cu_seqlens, max_seqlen: 
         scale = d ** -0.5
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    else:
+        _check_buffer("out", out, q.device, torch.bfloat16, q.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
-    elif lse is not None and (lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous fp32 tensor [H, T]")
+    elif lse is not None:
+        _check_buffer("lse", lse, q.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_fwd_blocksparse_fp8pv(
@@ -426,15 +449,18 @@ def pfa_attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None, want_lse: bool = 
     if o_b.shape != o_a.shape:
         raise ValueError("o_a and o_b must have the same shape")
     T, H, d = o_a.shape
+    if o_b.device != o_a.device:
+        raise ValueError(f"o_b must be on {o_a.device}")
     for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
-        if t.shape != (H, T) or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous fp32 CUDA tensor [H, T]")
+        _check_buffer(name, t, o_a.device, torch.float32, (H, T))
     if out is None:
         out = torch.empty_like(o_a)
-    elif out.shape != o_a.shape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bf16 tensor shaped like o_a")
+    else:
+        _check_buffer("out", out, o_a.device, torch.bfloat16, o_a.shape)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=o_a.device)
+    elif lse is not None:
+        _check_buffer("lse", lse, o_a.device, torch.float32, (H, T))
     if stream is None:
         stream = torch.cuda.current_stream(o_a.device)
     rc = _lib.load().pfa_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), T, H, d,
@@ -458,21 +484,23 @@ def pfa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int,
             raise ValueError(f"{name} must have q's shape")
     _check_table("cu_seqlens", cu_seqlens, torch)
     T, H, d = q.shape
-    if lse is None or lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    if lse is None:
         raise ValueError("lse must be the forward's contiguous fp32 [H, T]")
+    _check_buffer("lse", lse, q.device, torch.float32, (H, T))
     if scale is None:
         scale = d ** -0.5
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_bf16(name, t, torch)
-        if t.shape != q.shape:
-            raise ValueError(f"{name} must have q's shape")
+        _check_buffer(name, t, q.device, torch.bfloat16, q.shape)
     if workspace is None:
         workspace = torch.empty((2, H, T), dtype=torch.float32, device=q.device)
-    elif workspace.numel() < 2 * H * T or workspace.dtype != torch.float32 or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous fp32 tensor of >= 2*H*T elements")
+    else:
+        _check_buffer("workspace", workspace, q.device, torch.float32, (2, H, T))
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     rc = _lib.load().pfa_varlen_bwd(

@@ -4,7 +4,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpfa.so")
+# PFA_LIB selects another build of the same sources (the sanitizer leg of the CPU tests
+# loads a copy whose host code carries address/undefined-behaviour sanitizers this way)
+LIB_PATH = os.environ.get("PFA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpfa.so")
 
 # Every symbol include/pfa.h declares, with its ctypes signature.
 _SIGNATURES = {

@@ -26,19 +26,26 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (need ROCm with gfx950 support)")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, sanitize_host: bool = False, path: str | None = None) -> str:
+    """sanitize_host: compile the host code (argument checks, validators, launch setup)
+    with AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as always.
+    Loading such a library needs clang's ASan runtime preloaded.  path: output file."""
+    out = path or LIB
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-fvisibility=hidden", "-fno-honor-nans", "-I", INCLUDE, "-I", CSRC,
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           *SRCS, "-o", tmp]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    if sanitize_host:
+        cmd += ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+                "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+    cmd += [*SRCS, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

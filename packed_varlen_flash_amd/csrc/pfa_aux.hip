@@ -241,7 +241,8 @@ PFA_API int pfa_quantize_v_fp8(const void* v, const int32_t* cu_seqlens, int num
   for (const void* in : ins)
     if (in == v8 || in == static_cast<const void*>(v_scale)) return PFA_ERR_ALIAS;
   if (v8 == static_cast<const void*>(v_scale)) return PFA_ERR_ALIAS;
-  if (misaligned16(v) || (reinterpret_cast<uintptr_t>(v8) & 7) != 0 || (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0)
+  if (misaligned16(v) || (reinterpret_cast<uintptr_t>(v8) & 7) != 0 || misaligned4(v_scale) ||
+      misaligned4(cu_seqlens))
     return PFA_ERR_ALIGN;
   if ((int64_t)heads * head_dim > kMaxRowElems || (int64_t)num_seqs * heads * head_dim > INT32_MAX)
     return PFA_ERR_SIZE;
@@ -283,6 +284,10 @@ PFA_API int pfa_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
         (in == static_cast<const void*>(out) && (in == lse_a || in == lse_b)) ||
         (lse != nullptr && in == static_cast<const void*>(lse) && (in == o_a || in == o_b)))
       return PFA_ERR_ALIAS;
+  // O rows move in 16-byte chunks
+  if (misaligned16(o_a) || misaligned16(o_b) || misaligned16(out) || misaligned4(lse_a) ||
+      misaligned4(lse_b) || misaligned4(lse))
+    return PFA_ERR_ALIGN;
   if (total == 0) return PFA_OK;
   const int64_t chunks = total * heads * (head_dim / 8);
   const int64_t blocks = (chunks + kMergeThreads - 1) / kMergeThreads;

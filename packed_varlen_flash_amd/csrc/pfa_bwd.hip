@@ -574,6 +574,11 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
     for (int b = a + 1; b < 4; ++b)
       if (outs[a] == outs[b]) return PFA_ERR_ALIAS;
   }
+  // the [T, H, d] tensors move in 16-byte vectors; lse, workspace and the table element-wise
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned16(dout) ||
+      misaligned16(dq) || misaligned16(dk) || misaligned16(dv) || misaligned4(lse) || misaligned4(workspace) ||
+      misaligned4(cu_seqlens))
+    return PFA_ERR_ALIGN;
   const int64_t tiles_max = ((int64_t)max_seqlen + kBwdRows - 1) / kBwdRows;
   const int64_t slots = (int64_t)num_seqs * heads * tiles_max;
   if ((int64_t)heads * head_dim > kMaxRowElems || slots > INT32_MAX) return PFA_ERR_SIZE;

@@ -171,5 +171,7 @@ int device_cus(int* dev_out, int* cus_out) {
 }
 
 inline bool misaligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+// fp32 and int32 arrays are read and written one element at a time
+inline bool misaligned4(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3) != 0; }
 
 }  // namespace

@@ -9,16 +9,13 @@
 // running row maximum and normaliser, rescale and accumulate the output, and write only
 // the final output (and here the log-sum-exp) back to HBM.
 //
-// gfx950 mapping (both head sizes: one workgroup = 8 wave64s on one CU, two per SIMD):
-//   * work unit = (segment, head, 256-row query tile); a tile never spans two segments.
+// gfx950 mapping (d = 128: one workgroup = 8 wave64s on one CU, two waves per SIMD;
+// d = 64: 4 wave64s):
+//   * work unit = (segment, head, BM-row query tile); a tile never spans two segments.
 //     Tiles are listed longest segment first and handed out round-robin by a persistent
 //     grid; each XCD receives contiguous runs of the list so the query tiles that share
 //     one (segment, head) K/V stream sit behind the same L2.
-//   * each wave owns 32 queries and keeps their Q fragments in VGPRs.
-//   * the two waves of a SIMD belong to different groups, one slot apart: while one runs
-//     the MFMAs of a stage (QK of the next stage, PV of the current one), the other runs
-//     the softmax of a stage on the vector ALU, and they swap at the next workgroup
-//     barrier, so the matrix cores and the VALU work side by side.
+//   * each wave owns QB blocks of 32 queries and keeps their Q fragments in VGPRs.
 //   * K and V stages of 64 keys are double-buffered in LDS, loaded global -> LDS directly
 //     by buffer loads bounded at the segment end, so rows past it read as zeros and no
 //     neighbouring segment is ever touched.
@@ -33,7 +30,6 @@
 //     query and key tables; q, k, v read through row strides from a fused projection
 //     output (q rotated on load); listed key blocks only; P.V in FP8; listed key blocks
 //     with P.V in FP8.  The modes share the tile routine and differ only where noted.
-#include <type_traits>
 #include <vector>
 
 #include "pfa_common.h"
@@ -45,10 +41,7 @@ namespace {
 // exactly 1 and carries no bf16 rounding; a positive slack saves rescales (about 5% on
 // 4096-token segments) but leaves that weight rounded, which on sharp softmax rows pushes
 // the worst output error past 1e-2 of the exact result.
-#ifndef PFA_RESCALE_SLACK
-#define PFA_RESCALE_SLACK 0.0f
-#endif
-constexpr float kRescaleSlack = PFA_RESCALE_SLACK;
+constexpr float kRescaleSlack = 0.0f;
 
 struct Params {
   const __bf16* q;
@@ -99,38 +92,24 @@ __device__ constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int kSparseMaxBlocks = 1024;
 constexpr int kSparseLdsBytes = (kSparseMaxBlocks + 4) * 4;
 
-#ifndef PFA_LOAD_ALL
-#define PFA_LOAD_ALL 1
-#endif
-
-// Workgroup geometry at both head sizes: 8 wave64s, wave w owns query rows 32w .. 32w+31 of
-// a 256-row tile.  The hardware places wave w on SIMD w % 4, so waves 0-3 (group 0) and
-// 4-7 (group 1) put one wave of each group on every SIMD.  Keys come in 64-key stages.
-template <int D>
+// D: head_dim; QB: 32-query blocks per wave; NW: waves per workgroup; SK: keys per LDS
+// stage (a multiple of 64).
+template <int D, int QB, int NW = 4, int SK = 64>
 struct Tile {
-  static constexpr int NW = 8;
   static constexpr int THREADS = kWave * NW;
-  static constexpr int BM = NW * 32;                // query rows per workgroup tile
-  static constexpr int SK = 64;                     // keys per LDS stage
+  static constexpr int BM = NW * QB * 32;           // query rows per workgroup tile
   static constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  static constexpr int TILE_BYTES = SK * D * 2;     // one K (or V) stage
-  static constexpr int NCH = SK * CPR;              // 16-byte chunks of one stage
-  static constexpr int CPT = NCH / THREADS;         // ... per thread
-  static constexpr int NCH8 = SK * D / 16;          // 16-byte chunks of one e4m3 V stage
-  // Stage loads are issued by the waves of one group (the one in its softmax step at
-  // the even slots where loads go out), or by all waves with PFA_LOAD_ALL.
-  static constexpr int LW = PFA_LOAD_ALL ? NW : NW / 2;   // loading waves
-  static constexpr int CPL = NCH / (LW * kWave);           // bf16 chunks per loading lane
-  static constexpr int CPL8 = NCH8 >= LW * kWave ? NCH8 / (LW * kWave) : 1;   // e4m3 chunks
+  static constexpr int TILE_BYTES = SK * D * 2;     // one K (or V) stage, unpadded
+  static constexpr int CPT = SK * CPR / THREADS;    // chunks per thread per stage
   static constexpr int DT = D / 32;                 // 32-row output tiles along head_dim
   static constexpr int KSTEP = D / 16;              // 16-deep steps of the Q.K contraction
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
-  static constexpr int RING_BYTES = 2 * TILE_BYTES; // two-slot K ring; the V ring follows
-  static constexpr size_t LDS_BYTES = (size_t)2 * RING_BYTES + sizeof(int) * SCHED_INTS;
-  static_assert(CPT * THREADS == NCH, "stage must split evenly");
-  static_assert(NCH8 % kWave == 0 && NCH8 <= THREADS, "e4m3 stage in whole waves");
-  static_assert(sizeof(int) * kSortMax <= (size_t)RING_BYTES, "len scratch fits");
-  static_assert(4 * 32 * D * 2 <= RING_BYTES, "a group's output blocks fit one ring");
+  static constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 V row
+  static constexpr int CPT8 = SK * CPR8 / THREADS;  // e4m3 V chunks per thread per stage
+  static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
+  static_assert(CPT * THREADS == SK * CPR, "stage must split evenly");
+  static_assert(SK % kHalf == 0, "stages hold whole 64-key halves");
+  static_assert(sizeof(int) * kSortMax <= (size_t)kStages * TILE_BYTES, "len scratch fits");
 };
 
 // LDS layout of an e4m3 V stage: rows of D bytes (one key each), 16-byte chunks XORed
@@ -163,54 +142,198 @@ __device__ __forceinline__ float partner_sum(float x) {
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
-// Register arithmetic is free to move across a workgroup barrier (the barrier orders
-// memory only).  An empty volatile asm that takes a value as in/out operand keeps its
-// computation on this side of the next barrier: the step that produced it stays in its
-// slot instead of sinking into the next one.
-template <typename T>
-__device__ __forceinline__ void pin(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
-// Workgroup barrier without a memory fence.  __syncthreads() adds one, and since the
-// global -> LDS stage loads count as outstanding LDS writes, its fence waits for every
-// load in flight, including those issued in the slot that just started and not needed for
-// two more slots.  The slot loop waits for exactly the loads it needs (s_waitcnt before
-// the barrier of every even slot) and consumes every LDS read of a step inside that step,
-// so the plain barrier suffices; the memory clobber keeps the compiler from moving LDS
-// accesses across it.
-__device__ __forceinline__ void slot_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
 // ---------------------------------------------------------------------------------
-// One query tile of one (segment, head): the per-wave state and the two kinds of step.
+// One query tile of one (segment, head).
 //
-// Every wave alternates two kinds of step, one per "slot" (the time between two workgroup
-// barriers):
-//   MFMA step j:  S_{j+1}^T = K_{j+1} Q^T (QK of the next stage) and O^T += V_j^T P_j^T
-//                 (PV of the current one): 32 MFMAs at d = 128, their LDS reads, no VALU;
-//   softmax step j:  mask, row max, rescale decision (and O rescale) and the weights P_j
-//                 of stage j from S_j: VALU only.
-// Group 1 runs one slot behind group 0, so in every slot each SIMD holds one wave in an
-// MFMA step and one in a softmax step, and the matrix cores and the vector ALU work side
-// by side.  In lockstep (both waves of a SIMD in the same kind of step, which a barrier
-// per stage brings about) the two pipes mostly take turns.
+// Keys are consumed in 64-key LDS stages held in a ring of kStages slots.  Per stage the
+// wave computes both 32-key sub-blocks of S^T = K Q^T, runs one softmax head over the 64
+// keys (mask, max, rescale decision), then the weights of sub-block 0, its PV product,
+// the weights of sub-block 1 interleaved with that product's MFMAs, and the second PV.
+// The loads of stage s+1 are issued right after the barrier that opens stage s, into the
+// slot whose last readers that barrier retired.
 // ---------------------------------------------------------------------------------
-template <int D>
+template <int D, int QB>
 struct TileState {
-  bf16x8 qr[D / 16];             // Q fragments (B operand of K Q^T)
-  f32x16 o[D / 32];              // O^T accumulators
-  float m_run;                   // running max (base-2 scaled)
-  float l_run;                   // row sum of the fp32 weights (gives the LSE; normalises FP8 O)
-  float l_rnd;                   // row sum of the bf16 weights (normalises bf16 O)
+  using C = Tile<D, QB>;
+  bf16x8 qr[QB][C::KSTEP];       // Q fragments (B operand of K Q^T)
+  f32x16 o[QB][C::DT];           // O^T accumulators
+  float m_run[QB];               // running max (base-2 scaled)
+  float l_run[QB];               // row sum of the fp32 weights (gives the LSE; normalises FP8 O)
+  float l_rnd[QB];               // row sum of the bf16 weights (normalises bf16 O)
 };
 
-// V^T operand of output tile dt, 16-key step cc of the 32-key sub-block at vst: two
-// transposed reads 8 rows apart (voff[dt]: this lane's offset for rows 4g + i16/4).
+// S^T (keys x queries) = K Q^T for both 32-key sub-blocks of a stage, the two accumulator
+// chains interleaved so consecutive MFMAs never depend on each other.
+template <int D, int QB>
+__device__ __forceinline__ void qk_mfma(const bf16x8 (&ka)[D / 16], const bf16x8 (&kb)[D / 16],
+                                        const bf16x8 (&qr)[QB][D / 16], f32x16 (&s0)[QB],
+                                        f32x16 (&s1)[QB]) {
+#pragma unroll
+  for (int b = 0; b < QB; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[b][i] = 0.f;
+      s1[b][i] = 0.f;
+    }
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      s0[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], qr[b][t], s0[b], 0, 0, 0);
+      s1[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t], qr[b][t], s1[b], 0, 0, 0);
+    }
+}
+
+#ifndef PFA_QK_AHEAD_64
+#define PFA_QK_AHEAD_64 0
+#endif
+#ifndef PFA_QK_AHEAD_128
+#define PFA_QK_AHEAD_128 4
+#endif
+
+// Order of the QK phase of a stage: the two K operand reads of each 16-deep step (one per
+// 32-key sub-block) are issued `ahead` steps before the 2 QB MFMAs that consume them; left
+// to itself the compiler waits on each pair right before its MFMAs.
+template <int D, int QB>
+__device__ __forceinline__ void qk_schedule() {
+  constexpr int ahead = D == 128 ? PFA_QK_AHEAD_128 : PFA_QK_AHEAD_64;
+  static_assert(ahead >= 0 && ahead < D / 16, "prefetch distance within the contraction");
+  if constexpr (ahead > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * ahead, 0);
+#pragma unroll
+    for (int t = 0; t < D / 16 - ahead; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * QB * ahead, 0);
+  }
+}
+
+// V^T operand fragments of one sub-block: vst points at its first row; voff[dt] is this
+// lane's byte offset for the transposed read of rows 4g + i16/4 at d = 32dt + 16hh +
+// 4(i16 & 3); the second read of each pair is 8 rows further.
 template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const char* vst, int voff) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vst + voff));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vst + voff + 8 * D * 2));
-  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ void v_operands(const char* vst, const int (&voff)[D / 32],
+                                           bf16x8 (&va)[2][D / 32]) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const char* vp = vst + cc * 16 * D * 2 + voff[dt];
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * D * 2));
+      va[cc][dt] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+}
+
+// O^T += V^T P^T for one sub-block, 16 keys per MFMA.
+template <int D, int QB>
+__device__ __forceinline__ void pv_mfma(TileState<D, QB>& st, const bf16x8 (&va)[2][D / 32],
+                                        const bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        st.o[b][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc][dt], pb[b][cc], st.o[b][dt], 0, 0, 0);
+}
+
+// Online softmax head over a whole 64-key stage (both sub-blocks): one max, one rescale
+// decision.  No weights are pending when it runs, so O is rescaled in place.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_head64(TileState<D, QB>& st, f32x16 (&s0)[QB],
+                                               f32x16 (&s1)[QB], int key0, int L, float c, int g) {
+  using C = Tile<D, QB>;
+  if (key0 + 64 > L) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        if (key >= L) s0[b][i] = -INFINITY;
+        if (key + 32 >= L) s1[b][i] = -INFINITY;
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    float mx = fmaxf(s0[b][0], s0[b][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s0[b][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[b][i]);
+    mx = partner_max(mx);
+    const float mb = mx * c;
+    if (__builtin_amdgcn_ballot_w64(mb > st.m_run[b] + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(st.m_run[b], mb);
+      const float a = __builtin_amdgcn_exp2f(st.m_run[b] - m_new);
+      st.m_run[b] = m_new;
+      st.l_run[b] *= a;
+      st.l_rnd[b] *= a;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[b][dt][i] *= a;
+    }
+  }
+}
+
+// Online softmax, second half (straight-line): P = 2^(s*c - m) as bf16 B operands and two
+// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of bf16-rounded weights
+// can carry up to 2^-8 relative error, 3.9e-3, into the LSE of a sharp row).  l_rnd adds
+// the bf16 weights the PV product actually uses and normalises O: each weight's rounding
+// then enters numerator and denominator alike, so the error is sum_j dp_j (v_j - O) / l
+// rather than sum_j dp_j v_j / l.  That matters on rows with few keys and large, similar
+// values (|O| in [2, 4), where bf16 rounding of O already takes 2^-7 of the 1e-2 bar);
+// normalising by l_run there was measured past the bar.  Both sums chain straight into
+// their running values (one add, resp. one bf16 dot of a weight pair, per step).
+template <int D, int QB>
+__device__ __forceinline__ void softmax_body(TileState<D, QB>& st, const f32x16 (&s)[QB],
+                                             bf16x8 (&pb)[QB][2], float c) {
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float neg_m = -st.m_run[b];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[b][i], c, neg_m));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 1], c, neg_m));
+      st.l_run[b] += e0;
+      st.l_run[b] += e1;
+      const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+      st.l_rnd[b] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, st.l_rnd[b], false);
+      pb[b][i >> 3][i & 7] = pr[0];
+      pb[b][i >> 3][(i & 7) + 1] = pr[1];
+    }
+  }
+}
+
+// FP8 variant of softmax_body: weights w = 2^(s c - m + 8) rounded to e4m3 (nearest even)
+// four to a register, sub-block `half` filling bytes 16 half .. 16 half + 15 of the P^T
+// operand in the order of the accumulator elements; l_run adds the unrounded weights,
+// which also normalise O.
+template <int D, int QB>
+__device__ __forceinline__ void softmax_body8(TileState<D, QB>& st, const f32x16 (&s)[QB],
+                                              i32x8 (&pw)[QB], int half, float c) {
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float off = kP8Log2 - st.m_run[b];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[b][i], c, off));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 1], c, off));
+      const float e2 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 2], c, off));
+      const float e3 = __builtin_amdgcn_exp2f(fmaf(s[b][i + 3], c, off));
+      st.l_run[b] += e0;
+      st.l_run[b] += e1;
+      st.l_run[b] += e2;
+      st.l_run[b] += e3;
+      int w = 0;
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, w, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
+      pw[b][half * 4 + (i >> 2)] = w;
+    }
+  }
 }
 
 // The V^T operand of one 32-channel output tile for all 64 keys of a stage (e4m3): byte
@@ -228,171 +351,85 @@ __device__ __forceinline__ i32x8 v8_operand(const char* vst, int voff8) {
   return a;
 }
 
-#ifndef PFA_MFMA_PRIO
-#define PFA_MFMA_PRIO 2
-#endif
-#ifndef PFA_PV_AHEAD
-#define PFA_PV_AHEAD 2
-#endif
-
-// MFMA step (bf16 P.V).  QK: whether a next stage exists.  kst: K stage j+1 (both 32-key
-// sub-blocks, koff[t] = this lane's offset of row n32, chunk 2t+g); vst: V stage j.  The
-// 2 D/16 QK MFMAs and as many PV MFMAs alternate two and two; every accumulator chain
-// has at least three independent MFMAs between two of its links.  LDS reads run
-// PFA_PV_AHEAD contraction steps ahead of the MFMAs that use them.
-template <int D, bool QK>
-__device__ __forceinline__ void mfma_step(TileState<D>& st, f32x16& s0, f32x16& s1, const bf16x8 (&pb)[2][2],
-                                          const char* __restrict__ kst, const char* __restrict__ vst,
-                                          const int (&koff)[D / 16], const int (&voff)[D / 32]) {
-  constexpr int KS = D / 16, DT = D / 32;
-  if constexpr (QK) {
+// One 64-key stage of the FP8 variant: QK and the softmax head as in stage_body, then the
+// weights of both sub-blocks (e4m3) and one 32x32x64 FP8 MFMA per output tile.
+template <int D, int QB, int SK, typename IssueFn>
+__device__ __forceinline__ void stage_body_fp8(TileState<D, QB>& st, char* __restrict__ knext,
+                                               char* __restrict__ vnext, const char* __restrict__ kcur,
+                                               const char* __restrict__ vcur, bool issue,
+                                               const IssueFn& issue_fn, int s, int kbase, int L,
+                                               const int (&koff)[D / 16], const int (&voff8)[D / 32],
+                                               float c, int g) {
+  static_assert(SK == kHalf, "one 64-key head per stage");
+  if (issue) issue_fn(knext, vnext, s + 1);
+  f32x16 s0[QB], s1[QB];
+  i32x8 pw[QB];
+  bf16x8 ka[D / 16], kb[D / 16];
+  k_operands<D>(kcur, koff, ka);
+  k_operands<D>(kcur + 32 * D * 2, koff, kb);
+  qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
+  qk_schedule<D, QB>();
+  softmax_head64<D, QB>(st, s0, s1, kbase, L, c, g);
+  softmax_body8<D, QB>(st, s0, pw, 0, c);
+  i32x8 va[D / 32];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
-    }
-  }
+  for (int dt = 0; dt < D / 32; ++dt) va[dt] = v8_operand<D>(vcur, voff8[dt]);
+  softmax_body8<D, QB>(st, s1, pw, 1, c);
 #pragma unroll
-  for (int t = 0; t < KS; ++t) {
-    if constexpr (QK) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kst + 32 * D * 2 + koff[t]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qr[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, st.qr[t], s1, 0, 0, 0);
-    }
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int i = 2 * t + e;                 // sub-block i / (2 DT), key step (i / DT) & 1, tile i % DT
-      const int sub = i / (2 * DT), cc = (i / DT) & 1, dt = i % DT;
-      const bf16x8 va = v_operand<D>(vst + sub * 32 * D * 2 + cc * 16 * D * 2, voff[dt]);
-      st.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[sub][cc], st.o[dt], 0, 0, 0);
-    }
-  }
-  // order: the reads of PFA_PV_AHEAD steps first, then per step its MFMAs and the reads
-  // of the step PFA_PV_AHEAD further on
-  constexpr int RD = QK ? 6 : 4;   // LDS reads per step: 2 K rows (QK only) + 4 transposed V
-  constexpr int MF = QK ? 4 : 2;   // MFMAs per step
-  constexpr int AH = PFA_PV_AHEAD < KS ? PFA_PV_AHEAD : KS - 1;
-  __builtin_amdgcn_sched_group_barrier(0x100, RD * AH, 0);
-#pragma unroll
-  for (int t = 0; t < KS - AH; ++t) {
-    __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, MF * AH, 0);
+    for (int b = 0; b < QB; ++b)
+      st.o[b][dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[dt], pw[b], st.o[b][dt], 0, 0, 0, 0,
+                                                                   0, 0);
 }
 
-// MFMA step with P.V in FP8: the QK of mfma_step, then one 32x32x64 FP8 MFMA per output
-// tile over all 64 keys (weights pw from softmax_body8, V^T from the e4m3 stage).
-template <int D, bool QK>
-__device__ __forceinline__ void mfma_step8(TileState<D>& st, f32x16& s0, f32x16& s1, const i32x8& pw,
-                                           const char* __restrict__ kst, const char* __restrict__ vst,
-                                           const int (&koff)[D / 16], const int (&voff8)[D / 32]) {
-  constexpr int KS = D / 16, DT = D / 32;
-  if constexpr (QK) {
+// Interleave n MFMAs with the VALU work around them, `valu` VALU instructions after each.
+template <int N, int VALU>
+__device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s0[i] = 0.f;
-      s1[i] = 0.f;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < KS; ++t) {
-    if constexpr (QK) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kst + koff[t]);
-      const bf16x8 kb = *reinterpret_cast<const bf16x8*>(kst + 32 * D * 2 + koff[t]);
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, st.qr[t], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, st.qr[t], s1, 0, 0, 0);
-    }
-    if (t % 2 == 1) {
-      const int dt = t / 2;
-      const i32x8 va = v8_operand<D>(vst, voff8[dt]);
-      st.o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pw, st.o[dt], 0, 0, 0, 0, 0, 0);
-    }
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
   }
 }
 
-// Softmax step, first part, over a whole 64-key stage (both sub-blocks): key mask on the
-// segment's last stage, row max, one rescale decision.  O is rescaled in place: the
-// wave's MFMAs that accumulate into it ran in its previous slot.
-template <int D>
-__device__ __forceinline__ void softmax_head64(TileState<D>& st, f32x16& s0, f32x16& s1, int key0, int L,
-                                               float c, int g, float slack) {
-  if (key0 + 64 > L) {
+// One stage of keys kbase .. kbase + SK - 1: issue the next stage's loads into its slot,
+// then QK, softmax and PV on the current slot.  The four LDS pointers are restrict-qualified: the next slot and
+// the current slot never overlap, which lets the compiler keep the current slot's reads
+// from waiting on the next slot's loads.  The straight-line half of each sub-block's
+// softmax shares a basic block with the MFMAs of the neighbouring sub-block (QK of the
+// next, PV of the previous), so the MFMA pipe and the VALU work side by side.
+template <int D, int QB, int SK, typename IssueFn>
+__device__ __forceinline__ void stage_body(TileState<D, QB>& st, char* __restrict__ knext,
+                                           char* __restrict__ vnext, const char* __restrict__ kcur,
+                                           const char* __restrict__ vcur, bool issue,
+                                           const IssueFn& issue_fn, int s, int kbase, int L,
+                                           const int (&koff)[D / 16], const int (&voff)[D / 32],
+                                           float c, int g) {
+  constexpr int NQK = QB * D / 16;   // MFMAs of one sub-block's QK (and of its PV)
+  if (issue) issue_fn(knext, vnext, s + 1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key0 + (i >> 2) * 8 + 4 * g + (i & 3);
-      if (key >= L) s0[i] = -INFINITY;
-      if (key + 32 >= L) s1[i] = -INFINITY;
-    }
-  }
-  float mx = fmaxf(s0[0], s0[1]);
-#pragma unroll
-  for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s0[i]);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s1[i]);
-  mx = partner_max(mx);
-  const float mb = mx * c;
-  if (__builtin_amdgcn_ballot_w64(mb > st.m_run + slack) != 0) {
-    const float m_new = fmaxf(st.m_run, mb);
-    const float a = __builtin_amdgcn_exp2f(st.m_run - m_new);
-    st.m_run = m_new;
-    st.l_run *= a;
-    st.l_rnd *= a;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) st.o[dt][i] *= a;
-  }
-}
-
-// Softmax step, second part (straight-line): P = 2^(s*c - m) as bf16 B operands and two
-// row sums.  l_run adds the fp32 weights and gives the LSE (a sum of bf16-rounded weights
-// can carry up to 2^-8 relative error, 3.9e-3, into the LSE of a sharp row).  l_rnd adds
-// the bf16 weights the PV product actually uses and normalises O: each weight's rounding
-// then enters numerator and denominator alike, so the error is sum_j dp_j (v_j - O) / l
-// rather than sum_j dp_j v_j / l.  That matters on rows with few keys and large, similar
-// values (|O| in [2, 4), where bf16 rounding of O already takes 2^-7 of the 1e-2 bar);
-// normalising by l_run there was measured past the bar.  Both sums chain straight into
-// their running values (one add, resp. one bf16 dot of a weight pair, per step).
-template <int D>
-__device__ __forceinline__ void softmax_body(TileState<D>& st, const f32x16& s, bf16x8 (&pb)[2], float c) {
-  const float neg_m = -st.m_run;
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, neg_m));
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, neg_m));
-    st.l_run += e0;
-    st.l_run += e1;
-    const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-    st.l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, st.l_rnd, false);
-    pb[i >> 3][i & 7] = pr[0];
-    pb[i >> 3][(i & 7) + 1] = pr[1];
-  }
-}
-
-// FP8 variant of softmax_body: weights w = 2^(s c - m + 8) rounded to e4m3 (nearest even)
-// four to a register, sub-block `half` filling bytes 16 half .. 16 half + 15 of the P^T
-// operand in the order of the accumulator elements; l_run adds the unrounded weights,
-// which also normalise O.
-template <int D>
-__device__ __forceinline__ void softmax_body8(TileState<D>& st, const f32x16& s, i32x8& pw, int half,
-                                              float c) {
-  const float off = kP8Log2 - st.m_run;
-#pragma unroll
-  for (int i = 0; i < 16; i += 4) {
-    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[i], c, off));
-    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[i + 1], c, off));
-    const float e2 = __builtin_amdgcn_exp2f(fmaf(s[i + 2], c, off));
-    const float e3 = __builtin_amdgcn_exp2f(fmaf(s[i + 3], c, off));
-    st.l_run += e0;
-    st.l_run += e1;
-    st.l_run += e2;
-    st.l_run += e3;
-    int w = 0;
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, w, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, w, true);
-    pw[half * 4 + (i >> 2)] = w;
+  for (int half = 0; half < SK / kHalf; ++half) {
+    const int key0 = kbase + half * kHalf;     // first key of this half (kbase: of the stage)
+    if (half > 0 && key0 >= L) break;            // nothing left in this stage
+    const char* kh = kcur + half * kHalf * D * 2;
+    const char* vh = vcur + half * kHalf * D * 2;
+    f32x16 s0[QB], s1[QB];
+    bf16x8 p0[QB][2], p1[QB][2];
+    bf16x8 ka[D / 16], kb[D / 16];
+    bf16x8 va[2][D / 32];
+    k_operands<D>(kh, koff, ka);
+    k_operands<D>(kh + 32 * D * 2, koff, kb);
+    qk_mfma<D, QB>(ka, kb, st.qr, s0, s1);
+    qk_schedule<D, QB>();
+    softmax_head64<D, QB>(st, s0, s1, key0, L, c, g);
+    softmax_body<D, QB>(st, s0, p0, c);
+    v_operands<D>(vh, voff, va);
+    pv_mfma<D, QB>(st, va, p0);
+    softmax_body<D, QB>(st, s1, p1, c);
+    interleave_mfma_valu<NQK, 8 * 16 / NQK>();
+    v_operands<D>(vh + 32 * D * 2, voff, va);
+    pv_mfma<D, QB>(st, va, p1);
   }
 }
 
@@ -403,6 +440,7 @@ __device__ __forceinline__ void softmax_body8(TileState<D>& st, const f32x16& s,
 // even).  The DiT block of the Mage-Flow page (section on its fusion opportunities)
 // rotates q and k between the QKV projection and attention.
 __device__ __forceinline__ void rope_rotate(bf16x8& lo, bf16x8& hi, const float* cs, const float* sn) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs);
   const f32x4 c1 = *reinterpret_cast<const f32x4*>(cs + 4);
   const f32x4 s0 = *reinterpret_cast<const f32x4*>(sn);
@@ -421,26 +459,16 @@ __device__ __forceinline__ void rope_rotate(bf16x8& lo, bf16x8& hi, const float*
   hi = nhi;
 }
 
-// ---------------------------------------------------------------------------------
-// One query tile of one (segment, head).
-//
-// Stage j's K is read by the MFMA step j-1 (QK of stage j), its V by MFMA step j (PV).
-// With group 1 one slot behind group 0, K_j is read in slots 2j and 2j+1 and V_j in slots
-// 2j+2 and 2j+3.  Both rings have two slots.  At every even slot 2u, right after its
-// barrier, the workgroup issues K_{u+1} and V_u (global -> LDS, bounded at the segment
-// end); each lands in the ring slot whose last readers the barrier just retired, and has
-// two slots to arrive before its first reader.
-// ---------------------------------------------------------------------------------
 // MODE also keys the instantiation to its kernel variant (the HIP host pass rejects a
 // device template specialisation shared by two kernel templates' instantiations).
-template <int D, int MODE>
-__device__ __forceinline__ void process_tile(const Params& p, char* kring, char* vring, int* s_blk, int seg,
-                                             int qa, int Lq, int ka, int Lk, int h, int qt, int Tq) {
-  using C = Tile<D>;
+template <int D, int QB, int NW, int SK, int MODE>
+__device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16* vs, int* s_blk,
+                                             int seg, int qa, int Lq, int ka, int Lk, int h,
+                                             int qt, int Tq) {
+  using C = Tile<D, QB, NW, SK>;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-  const int grp = wave >> 2;         // 0: waves 0-3, 1: waves 4-7 (one slot behind)
   const int n32 = lane & 31;         // query column (S^T) / key row of the K operand
   const int g = lane >> 5;           // half-wave
   const int i16 = lane & 15;
@@ -454,14 +482,14 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
   const __bf16* kbase = p.k + (int64_t)ka * k_rs + head_off;
   const __bf16* vbase = p.v + (int64_t)ka * v_rs + head_off;
   const uint8_t* v8base = mode_fp8(MODE) ? p.v8 + (int64_t)ka * rs + head_off : nullptr;
-  const int q0 = qt * C::BM + wave * 32;
-  int ns = (Lk + C::SK - 1) / C::SK;       // stages (0 when the key segment is empty)
+  const int q0 = qt * C::BM + wave * (QB * 32);
+  int ns = (Lk + SK - 1) / SK;             // LDS stages (0 when the key segment is empty)
   const float c = p.c;
   if constexpr (mode_sparse(MODE)) {
     // The tile's list, compacted by wave 0 into LDS: entries outside the segment's key
     // blocks are dropped, the rest keep their order.  ns becomes the number kept.  (The
     // previous tile's last barrier retired every reader of the old list.)
-    static_assert(C::SK == 64, "key blocks are 64-key stages");
+    static_assert(SK == 64, "key blocks are 64-key stages");
     if (wave == 0) {
       const int64_t row = ((int64_t)seg * p.layout_heads + (p.layout_heads == 1 ? 0 : h)) * p.qt_max + qt;
       int e0 = 0, e1 = 0;
@@ -487,18 +515,19 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
   }
   // first key of stage i: consecutive 64-key stages, or the listed blocks in list order
   auto stage_key = [&](int i) {
-    if constexpr (mode_sparse(MODE)) return __builtin_amdgcn_readfirstlane(s_blk[i]) * C::SK;
-    else return i * C::SK;
+    if constexpr (mode_sparse(MODE)) return __builtin_amdgcn_readfirstlane(s_blk[i]) * SK;
+    else return i * SK;
   };
 
-  TileState<D> st;
-  {
-    const int row = q0 + n32;
+  TileState<D, QB> st;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const int row = q0 + b * 32 + n32;
 #pragma unroll
     for (int t = 0; t < C::KSTEP; ++t) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (row < Lq) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * q_rs + 16 * t + 8 * g);
-      st.qr[t] = __builtin_bit_cast(bf16x8, x);
+      st.qr[b][t] = __builtin_bit_cast(bf16x8, x);
     }
     if constexpr (MODE == kModeQkv) {
       // rotate-half RoPE: the lane's chunk t holds features 16t + 8g + 0..7 and chunk
@@ -507,18 +536,18 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
         const int64_t tab = (int64_t)(qa + row) * (D / 2);
 #pragma unroll
         for (int t = 0; t < C::KSTEP / 2; ++t)
-          rope_rotate(st.qr[t], st.qr[t + C::KSTEP / 2], p.rope_cos + tab + 16 * t + 8 * g,
+          rope_rotate(st.qr[b][t], st.qr[b][t + C::KSTEP / 2], p.rope_cos + tab + 16 * t + 8 * g,
                       p.rope_sin + tab + 16 * t + 8 * g);
       }
     }
+    st.m_run[b] = -INFINITY;
+    st.l_run[b] = 0.f;
+    st.l_rnd[b] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.o[b][dt][i] = 0.f;
   }
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
-  st.l_rnd = 0.f;
-#pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.o[dt][i] = 0.f;
 
   // ---- per-lane LDS offsets (fixed for the whole tile)
   int koff[C::KSTEP], voff[C::DT];
@@ -541,181 +570,90 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
   // ---- stage loads: global -> LDS directly (no registers).  Lane l of the wave's i-th
   // load writes physical chunk (wave*CPT + i)*64 + l, fetched from its logical source.
   // A buffer resource bounded at the segment end returns zeros for rows >= L, so no row
-  // of a neighbouring segment is ever read.  The host keeps 64 rows of every stride
-  // within int range.
+  // of a neighbouring segment is ever read.
+  // the host keeps 64 rows of every stride within int range
   const int kbytes = (int)(k_rs * 2);
   const int vbytes = (int)(v_rs * 2);
-  const bool loader = PFA_LOAD_ALL || grp == 1;
-  const int lw = PFA_LOAD_ALL ? wave : wave - C::NW / 2;   // index among the loading waves
-  int src_k[C::CPL], src_v[C::CPL];      // logical source offsets of this lane's chunks
+  char* const kring = reinterpret_cast<char*>(ks);
+  char* const vring = reinterpret_cast<char*>(vs);
+  int src_k[C::CPT], src_v[C::CPT];      // logical source offsets of this lane's chunks
 #pragma unroll
-  for (int i = 0; i < C::CPL; ++i) {
-    const int P = (lw * C::CPL + i) * 64 + lane;
+  for (int i = 0; i < C::CPT; ++i) {
+    const int P = (wave * C::CPT + i) * 64 + lane;
     src_k[i] = logical_src<D, Swz::K>(P, kbytes);
     if constexpr (mode_fp8(MODE)) {
-      if (i < C::CPL8) src_v[i] = logical_src8<D>((lw * C::CPL8 + i) * 64 + lane, (int)rs);
+      if (i < C::CPT8) src_v[i] = logical_src8<D>((wave * C::CPT8 + i) * 64 + lane, (int)rs);
     } else {
       src_v[i] = logical_src<D, Swz::V>(P, vbytes);
     }
   }
-  auto issue_k = [&](int stage) {
-    if (!loader) return;
+  auto issue_fn = [&](char* kdst, char* vdst, int stage) {
     const int kb = stage_key(stage);
-    const int rows = (Lk - kb < C::SK) ? (Lk - kb) : C::SK;
+    const int rows = (Lk - kb < SK) ? (Lk - kb) : SK;
     __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)kb * k_rs), 0, rows * kbytes, kRsrcFlags);
-    char* kdst = kring + (stage & 1) * C::TILE_BYTES + lw * C::CPL * 1024;
+    kdst += wave * C::CPT * 1024;
 #pragma unroll
-    for (int i = 0; i < C::CPL; ++i)
+    for (int i = 0; i < C::CPT; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kdst + i * 1024), 16, src_k[i], 0, 0, 0);
-  };
-  auto issue_v = [&](int stage) {
-    if (!loader) return;
-    const int kb = stage_key(stage);
-    const int rows = (Lk - kb < C::SK) ? (Lk - kb) : C::SK;
     if constexpr (mode_fp8(MODE)) {
-      if (lw * C::CPL8 * kWave < C::NCH8) {
-        __amdgpu_buffer_rsrc_t r8 = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(v8base + (int64_t)kb * rs), 0, rows * (int)rs, kRsrcFlags);
-        char* vdst = vring + (stage & 1) * C::TILE_BYTES + lw * C::CPL8 * 1024;
+      __amdgpu_buffer_rsrc_t r8 = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(v8base + (int64_t)kb * rs), 0, rows * (int)rs, kRsrcFlags);
+      vdst += wave * C::CPT8 * 1024;
 #pragma unroll
-        for (int i = 0; i < C::CPL8; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
-      }
+      for (int i = 0; i < C::CPT8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r8, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
     } else {
       __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)kb * v_rs), 0, rows * vbytes, kRsrcFlags);
-      char* vdst = vring + (stage & 1) * C::TILE_BYTES + lw * C::CPL * 1024;
+      vdst += wave * C::CPT * 1024;
 #pragma unroll
-      for (int i = 0; i < C::CPL; ++i)
+      for (int i = 0; i < C::CPT; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vdst + i * 1024), 16, src_v[i], 0, 0, 0);
     }
   };
-  // Start of slot t: at even slots the loads issued two slots earlier must have landed
-  // (each wave waits for its own, the barrier for everyone's); then the next go out.
-  auto slot = [&](int t) {
-    if ((t & 1) == 0 && t > 0 && loader) __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    slot_barrier();
-    if ((t & 1) == 0) {
-      const int u = t >> 1;
-      if (u + 1 < ns) issue_k(u + 1);
-      if (u < ns) issue_v(u);
-    }
-  };
 
-  f32x16 s0, s1;                  // scores of the stage after the current one
-  bf16x8 pb[2][2];                // bf16 weights of the current stage (B operands)
-  i32x8 pw;                       // FP8 variant: its e4m3 weights
-  auto pin_o = [&]() {
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) pin(st.o[dt]);
-  };
-  auto softmax_step = [&](int j) {
-    // FP8 weights must stay below 448: no slack there
-    softmax_head64<D>(st, s0, s1, stage_key(j), Lk, c, g, mode_fp8(MODE) ? 0.f : kRescaleSlack);
-    if constexpr (mode_fp8(MODE)) {
-      softmax_body8<D>(st, s0, pw, 0, c);
-      softmax_body8<D>(st, s1, pw, 1, c);
-      pin(pw);
-    } else {
-      softmax_body<D>(st, s0, pb[0], c);
-      softmax_body<D>(st, s1, pb[1], c);
-      pin(pb[0][0]);
-      pin(pb[0][1]);
-      pin(pb[1][0]);
-      pin(pb[1][1]);
-    }
-    pin(st.m_run);
-    pin(st.l_run);
-    pin(st.l_rnd);
-    pin_o();
-  };
-  // MFMA step j: K_{j+1} in K slot KS (when QK), V_j in V slot VS
-  auto step_mfma = [&](auto qk, auto kslot, auto vslot) {
-    constexpr bool QK = decltype(qk)::value;
-    const char* kst = kring + decltype(kslot)::value * C::TILE_BYTES;
-    const char* vst = vring + decltype(vslot)::value * C::TILE_BYTES;
-    // the wave in its MFMA step issues first: its partner's VALU fills the gaps between
-    // MFMAs instead of delaying them
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(PFA_MFMA_PRIO);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (mode_fp8(MODE)) mfma_step8<D, QK>(st, s0, s1, pw, kst, vst, koff, voff);
-    else mfma_step<D, QK>(st, s0, s1, pb, kst, vst, koff, voff);
-    if constexpr (QK) {
-      pin(s0);
-      pin(s1);
-    }
-    pin_o();
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-
-  if (ns > 0) {
-    issue_k(0);
-    if (loader) __builtin_amdgcn_s_waitcnt(kWaitVmem);
-    if (grp == 1) slot(0);
-    // QK of stage 0 (K slot 0): S_0
-    slot(grp);
-    {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s0[i] = 0.f;
-        s1[i] = 0.f;
-      }
-      bf16x8 ka[C::KSTEP], kb[C::KSTEP];
-      k_operands2<D>(kring, kring + 32 * D * 2, koff, ka, kb);
-#pragma unroll
-      for (int t = 0; t < C::KSTEP; ++t) {
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[t], st.qr[t], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[t], st.qr[t], s1, 0, 0, 0);
-      }
-      pin(s0);
-      pin(s1);
-    }
-    int j = 0;
-    for (; j + 2 < ns; j += 2) {      // stages j and j+1 both have a next stage
-      slot(2 * j + 1 + grp);
-      softmax_step(j);
-      slot(2 * j + 2 + grp);
-      step_mfma(T_{}, I1{}, I0{});
-      slot(2 * j + 3 + grp);
-      softmax_step(j + 1);
-      slot(2 * j + 4 + grp);
-      step_mfma(T_{}, I0{}, I1{});
-    }
-    slot(2 * j + 1 + grp);
-    softmax_step(j);
-    slot(2 * j + 2 + grp);
-    if (ns - j == 2) {
-      step_mfma(T_{}, I1{}, I0{});
-      slot(2 * j + 3 + grp);
-      softmax_step(j + 1);
-      slot(2 * j + 4 + grp);
-      step_mfma(F_{}, I0{}, I1{});
-    } else {
-      step_mfma(F_{}, I0{}, I0{});
-    }
-    if (grp == 0) slot(2 * ns + 1);
+  // ---- stage loop.  Stage s sits in slot s % 2; the loads of stage s+1 are issued
+  // right after the barrier that retires every reader of its slot, and have the whole of
+  // stage s to land.  Unrolled by two so both slot offsets are immediates.
+  static_assert(kStages == 2, "the stage loop alternates two slots");
+  // no keys, no loads: a zero-row stage would still zero-fill slot 0, which the epilogue
+  // reuses for the output
+  if (ns > 0) issue_fn(kring, vring, 0);
+  for (int s = 0; s < ns; s += 2) {
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __syncthreads();
+    if constexpr (mode_fp8(MODE))
+      stage_body_fp8<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+                                issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
+    else
+      stage_body<D, QB, SK>(st, kring + C::TILE_BYTES, vring + C::TILE_BYTES, kring, vring, s + 1 < ns,
+                            issue_fn, s, stage_key(s), Lk, koff, voff, c, g);
+    if (s + 1 >= ns) break;
+    __builtin_amdgcn_s_waitcnt(kWaitVmem);
+    __syncthreads();
+    if constexpr (mode_fp8(MODE))
+      stage_body_fp8<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+                                issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
+    else
+      stage_body<D, QB, SK>(st, kring, vring, kring + C::TILE_BYTES, vring + C::TILE_BYTES, s + 2 < ns,
+                            issue_fn, s + 1, stage_key(s + 1), Lk, koff, voff, c, g);
   }
+  __syncthreads();   // every wave has left the ring
 
   // ---- epilogue: O = acc / l_rnd (FP8: acc / l_run) in bf16 (round to nearest even),
-  // LSE = ln2 * (m + log2 l_run).  Group 0 finishes while group 1 runs its last MFMA step
-  // on the V ring, and stages its output in the K ring; group 1 follows after a barrier
-  // and stages in the V ring.  Each wave writes its 32 x D block into its own part of
-  // the ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
+  // LSE = ln2 * (m + log2 l_run).  O goes out through LDS: each wave writes its (QB*32) x D block into the free
+  // ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
   // consecutive rows, so 16 lanes store 256 contiguous bytes instead of every store
   // instruction touching 16-byte pieces of 32 different rows.
-  auto epilogue = [&](char* region) {
-    char* const ost = region + (wave & 3) * (32 * D * 2);
-    const float lt = partner_sum(st.l_run);
-    const float lr = mode_fp8(MODE) ? lt : partner_sum(st.l_rnd);
+  static_assert(NW * QB * 32 * D * 2 <= 2 * kStages * C::TILE_BYTES, "O staging fits the ring");
+  char* const ost = kring + wave * (QB * 32 * D * 2);
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float lt = partner_sum(st.l_run[b]);
+    const float lr = mode_fp8(MODE) ? lt : partner_sum(st.l_rnd[b]);
     const float inv = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
+    const int r = b * 32 + n32;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -727,47 +665,42 @@ __device__ __forceinline__ void process_tile(const Params& p, char* kring, char*
                                                      8 * ii + 4 * g);
         bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[dt][4 * ii + e] * sc[e]);
-        *reinterpret_cast<bf16x4*>(ost + phys_off<D, Swz::K>(n32, 4 * dt + ii) + 8 * g) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * sc[e]);
+        *reinterpret_cast<bf16x4*>(ost + phys_off<D, Swz::K>(r, 4 * dt + ii) + 8 * g) = w;
       }
-    const float mfix = mode_fp8(MODE) ? st.m_run - kP8Log2 : st.m_run;   // FP8 sums 2^8 p
-    if (p.lse != nullptr && g == 0 && q0 + n32 < Lq)
-      p.lse[(int64_t)h * Tq + qa + q0 + n32] = (mfix + __builtin_amdgcn_logf(lt)) * kLn2;
-    // the wave reads back only what it wrote
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    constexpr int OCH = 32 * C::CPR;      // 16-byte chunks of the wave's block
-    static_assert(OCH % kWave == 0, "whole chunk rows per lane");
-#pragma unroll
-    for (int k = 0; k < OCH / kWave; ++k) {
-      const int P = k * kWave + lane;
-      const int r = P / C::CPR;
-      const int ch = P % C::CPR;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, Swz::K>(r, ch));
-      if (q0 + r < Lq)
-        *reinterpret_cast<u32x4*>(p.out + (int64_t)(qa + q0 + r) * rs + head_off + ch * 8) = x;
-    }
-  };
-  if (grp == 0) epilogue(kring);
+    const float mfix = mode_fp8(MODE) ? st.m_run[b] - kP8Log2 : st.m_run[b];   // FP8 sums 2^8 p
+    if (p.lse != nullptr && g == 0 && q0 + r < Lq)
+      p.lse[(int64_t)h * Tq + qa + q0 + r] = (mfix + __builtin_amdgcn_logf(lt)) * kLn2;
+  }
   __syncthreads();
-  if (grp == 1) epilogue(vring);
-  // the next tile's first barrier retires the V-ring readers above before any V load
+  constexpr int OCH = QB * 32 * C::CPR;      // 16-byte chunks of the wave's block
+  static_assert(OCH % kWave == 0, "whole chunk rows per lane");
+#pragma unroll
+  for (int k = 0; k < OCH / kWave; ++k) {
+    const int P = k * kWave + lane;
+    const int r = P / C::CPR;
+    const int ch = P % C::CPR;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, Swz::K>(r, ch));
+    if (q0 + r < Lq)
+      *reinterpret_cast<u32x4*>(p.out + (int64_t)(qa + q0 + r) * rs + head_off + ch * 8) = x;
+  }
+  __syncthreads();   // the next tile's first stage overwrites the ring
 }
 
 // kModeCross: separate query and key tables; otherwise the key table is the query table
 // (known at compile time, so the key-side offsets and lengths fold into the query ones).
-template <int D, int MODE>
-__global__ void __launch_bounds__(kWave * Tile<D>::NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, int QB, int NW, int SK, int WPE, int MODE>
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 pfa_fwd_kernel(Params p) {
   const int32_t* const cu_k = MODE == kModeCross ? p.cu_k : p.cu_q;
-  using C = Tile<D>;
+  using C = Tile<D, QB, NW, SK>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  char* kring = reinterpret_cast<char*>(smem);
-  char* vring = kring + C::RING_BYTES;
-  int* s_order = reinterpret_cast<int*>(smem + 2 * C::RING_BYTES);
+  __bf16* ks = reinterpret_cast<__bf16*>(smem);
+  __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
+  int* s_order = reinterpret_cast<int*>(smem + 2 * kStages * C::TILE_BYTES);
   int* s_prefix = s_order + kSortMax;
   int* s_blk = s_order + C::SCHED_INTS;     // block-sparse variant only (its LDS is larger)
-  int* s_len = reinterpret_cast<int*>(kring);  // scratch, dead before the first K tile lands
+  int* s_len = reinterpret_cast<int*>(ks);  // scratch, dead before the first K tile lands
 
   const int Tq = p.cu_q[p.num_seqs];
   const int Tk = cu_k[p.num_seqs];
@@ -822,7 +755,7 @@ pfa_fwd_kernel(Params p) {
       if (Lk > Tk - ka) Lk = Tk - ka;
       if (Lk < 0) Lk = 0;
     }
-    process_tile<D, MODE>(p, kring, vring, s_blk, s, qa, Lq, ka, Lk, h, qt, Tq);
+    process_tile<D, QB, NW, SK, MODE>(p, ks, vs, s_blk, s, qa, Lq, ka, Lk, h, qt, Tq);
   }
 }
 
@@ -879,13 +812,13 @@ struct Variant {
   size_t lds;
 };
 
-template <int D, int MODE>
+template <int D, int QB, int NW, int SK, int WPE, int MODE>
 Variant make_variant() {
-  using C = Tile<D>;
-  static_assert(!mode_sparse(MODE) || (C::BM == PFA_SPARSE_BLOCK_Q && C::SK == PFA_SPARSE_BLOCK_K),
+  using C = Tile<D, QB, NW, SK>;
+  static_assert(!mode_sparse(MODE) || (C::BM == PFA_SPARSE_BLOCK_Q && SK == PFA_SPARSE_BLOCK_K),
                 "the block-sparse layout's blocks are the kernel's query tile and key stage");
-  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, MODE>), C::BM, C::THREADS,
-                 C::LDS_BYTES + (mode_sparse(MODE) ? kSparseLdsBytes : 0)};
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_kernel<D, QB, NW, SK, WPE, MODE>), C::BM,
+                 C::THREADS, C::LDS_BYTES + (mode_sparse(MODE) ? kSparseLdsBytes : 0)};
 }
 
 constexpr int kVariants = 12;  // head_dim 64, 128 x the six kernel modes
@@ -893,10 +826,35 @@ std::atomic<int> g_occ[kMaxDevices][kVariants];
 
 int variant_index(int head_dim, int mode) { return (head_dim == 64 ? 0 : 1) + 2 * mode; }
 
+#ifndef PFA_D64_QB
+#define PFA_D64_QB 2
+#endif
+#ifndef PFA_D64_WPE
+#define PFA_D64_WPE 2
+#endif
+#ifndef PFA_D128_QB
+#define PFA_D128_QB 1
+#endif
+#ifndef PFA_D128_WPE
+#define PFA_D128_WPE 2
+#endif
+#ifndef PFA_D64_NW
+#define PFA_D64_NW 4
+#endif
+#ifndef PFA_D128_NW
+#define PFA_D128_NW 8
+#endif
+#ifndef PFA_D64_SK
+#define PFA_D64_SK 64
+#endif
+#ifndef PFA_D128_SK
+#define PFA_D128_SK 64
+#endif
+
 template <int MODE>
 Variant variant_of(int head_dim) {
-  if (head_dim == 64) return make_variant<64, MODE>();
-  return make_variant<128, MODE>();
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, MODE>();
+  return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, MODE>();
 }
 
 Variant variant_for(int head_dim, int mode) {
@@ -993,6 +951,10 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const
   for (const void* in : ins)
     if (in == out || (lse != nullptr && in == static_cast<const void*>(lse))) return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
+  // q, k, v and out move in 16-byte vectors
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned4(lse) ||
+      misaligned4(cu_seqlens_q) || misaligned4(cu_seqlens_k))
+    return PFA_ERR_ALIGN;
   if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
 
   Params prm{};
@@ -1039,7 +1001,7 @@ PFA_API int pfa_varlen_fwd_qkv(const void* qkv, const float* rope_cos, const flo
     for (int b = a + 1; b < 3; ++b)
       if (outs[a] == outs[b]) return PFA_ERR_ALIAS;
   }
-  if (misaligned16(qkv) || misaligned16(out) ||
+  if (misaligned16(qkv) || misaligned16(out) || misaligned4(lse) || misaligned4(cu_seqlens) ||
       (rope && (misaligned16(k_rot) || misaligned16(rope_cos) || misaligned16(rope_sin))))
     return PFA_ERR_ALIGN;
   const int64_t hd = (int64_t)heads * head_dim;
@@ -1106,6 +1068,9 @@ PFA_API int pfa_varlen_fwd_blocksparse(const void* q, const void* k, const void*
     if (in != nullptr && (in == out || (lse != nullptr && in == static_cast<const void*>(lse))))
       return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
+  if (misaligned16(q) || misaligned16(k) || misaligned16(v) || misaligned16(out) || misaligned4(lse) ||
+      misaligned4(cu_seqlens) || misaligned4(kv_ptr) || misaligned4(kv_idx))
+    return PFA_ERR_ALIGN;
   if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
   if ((int64_t)max_seqlen > (int64_t)kSparseMaxBlocks * PFA_SPARSE_BLOCK_K) return PFA_ERR_SIZE;
   const int64_t qt_max = ((int64_t)max_seqlen + PFA_SPARSE_BLOCK_Q - 1) / PFA_SPARSE_BLOCK_Q;
@@ -1182,7 +1147,9 @@ PFA_API int pfa_varlen_fwd_fp8pv(const void* q, const void* k, const void* v8, c
   for (const void* in : ins)
     if (in == out || (lse != nullptr && in == static_cast<const void*>(lse))) return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
-  if (misaligned16(v8) || misaligned16(v_scale)) return PFA_ERR_ALIGN;
+  if (misaligned16(v8) || misaligned16(v_scale) || misaligned16(q) || misaligned16(k) || misaligned16(out) ||
+      misaligned4(lse) || misaligned4(cu_seqlens))
+    return PFA_ERR_ALIGN;
   if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
 
   Params prm{};
@@ -1222,7 +1189,9 @@ PFA_API int pfa_varlen_fwd_blocksparse_fp8pv(const void* q, const void* k, const
     if (in != nullptr && (in == out || (lse != nullptr && in == static_cast<const void*>(lse))))
       return PFA_ERR_ALIAS;
   if (lse != nullptr && static_cast<const void*>(lse) == out) return PFA_ERR_ALIAS;
-  if (misaligned16(v8) || misaligned16(v_scale)) return PFA_ERR_ALIGN;
+  if (misaligned16(v8) || misaligned16(v_scale) || misaligned16(q) || misaligned16(k) || misaligned16(out) ||
+      misaligned4(lse) || misaligned4(cu_seqlens) || misaligned4(kv_ptr) || misaligned4(kv_idx))
+    return PFA_ERR_ALIGN;
   if ((int64_t)heads * head_dim > kMaxRowElems) return PFA_ERR_SIZE;
   if ((int64_t)max_seqlen > (int64_t)kSparseMaxBlocks * PFA_SPARSE_BLOCK_K) return PFA_ERR_SIZE;
 

@@ -367,23 +367,27 @@ class WorkedExample:
 
 
 def worked_example() -> WorkedExample:
-    """Inputs of the jefxiong.cn SparseAttn article's section-4 experiment.
+    """Inputs of the worked experiment in section 4 of the jefxiong.cn SparseAttn article.
 
-    4 frames of 4x4 = 16 positions, n = 64 tokens in frame-major order, d = 4 + 16 = 20.
-    Head 0 carries a signal of 6 on the one-hot of the token's frame, head 1 on the
-    one-hot of its position (offset by the 4 frame dimensions); Gaussian noise of
-    standard deviation 0.15 is added to both heads, drawn first from
-    ``default_rng(7)``; keys equal queries; the shared values, drawn next, are
-    N(0, 1) of shape (64, 3).
+    The article describes a video of 4 frames on a 4 x 4 grid of positions, 64 tokens in
+    frame-major order, and two synthetic heads: in the first ("spatial") every token
+    carries a signal of strength 6 on a feature naming its frame, in the second
+    ("temporal") on a feature naming its position within the frame.  Features are one-hot:
+    the 4 frame features come first, then the 16 position features (d = 20).  Gaussian
+    noise of standard deviation 0.15 is added to both heads, keys equal queries, and the
+    values are standard normal of width 3, shared by both heads; the generator is
+    numpy's default_rng seeded with 7, the noise drawn before the values (the order that
+    reproduces the printed numbers).
     """
-    rng = np.random.default_rng(7)
     frames, positions = 4, 16
-    n, d = frames * positions, frames + positions
-    frame = np.repeat(np.arange(frames), positions)
-    pixel = np.tile(np.arange(positions), frames)
-    q = np.zeros((2, n, d), dtype=np.float64)
-    q[0, np.arange(n), frame] = 6.0
-    q[1, np.arange(n), frames + pixel] = 6.0
-    q = q + rng.normal(0.0, 0.15, size=q.shape)
-    v = rng.normal(size=(n, 3))
-    return WorkedExample(q=q, v=v, frame=frame, pixel=pixel, frames=frames, positions=positions)
+    order = [(f, p) for f in range(frames) for p in range(positions)]   # frame-major
+    frame = np.array([f for f, _ in order])
+    pixel = np.array([p for _, p in order])
+    features = np.eye(frames + positions)
+    # head 0 names the frame feature, head 1 the position feature after the frame block
+    signal = np.stack([6.0 * features[frame], 6.0 * features[frames + pixel]])
+    gen = np.random.default_rng(7)
+    noise = gen.normal(0.0, 0.15, size=signal.shape)
+    values = gen.standard_normal((len(order), 3))
+    return WorkedExample(q=signal + noise, v=values, frame=frame, pixel=pixel, frames=frames,
+                         positions=positions)

@@ -68,12 +68,19 @@ def compare(out_bits, lse, o_ref, l_ref):
     denom = float(np.sqrt(np.sum(o_ref * o_ref)))
     rel_rms = float(np.sqrt(np.sum(diff * diff)) / denom) if denom > 0 else 0.0
     lse_abs = float(np.abs(lse.astype(np.float64) - l_ref).max()) if lse is not None and lse.size else 0.0
+    # elements over the raw 1e-2 bar: they can pass only through the |O_ref| >= 4 allowance
+    n_over = int(np.count_nonzero(ad > MAX_ABS))
     return dict(max_abs=max_abs, max_abs_small=max_abs_small, excess_big=excess_big,
-                rel_rms=rel_rms, lse_abs=lse_abs, n_big=int(big.sum()))
+                rel_rms=rel_rms, lse_abs=lse_abs, n_big=int(big.sum()), n_over_raw_bar=n_over)
 
 
 def assert_parity(m, label=""):
-    say(f"[parity] {label}: max|err|={m['max_abs']:.3e} (|O_ref|<4: {m['max_abs_small']:.3e}; "
+    """Raw max|err| is printed against the 1e-2 bar as written; elements over it pass only
+    where |O_ref| >= 4 (bf16 rounding of the output alone can exceed 1e-2 there), and their
+    count is printed too, so a pass through the allowance is visible in the log."""
+    say(f"[parity] {label}: raw max|err|={m['max_abs']:.3e} (bar 1e-2; "
+        f"{m.get('n_over_raw_bar', 0)} elements over it, passing only via the |O_ref|>=4 allowance) "
+        f"(|O_ref|<4: {m['max_abs_small']:.3e}; "
         f"{m['n_big']} elements >=4, worst excess over rounding {m['excess_big']:.3e}) "
         f"relRMS={m['rel_rms']:.3e} LSE={m['lse_abs']:.3e}")
     assert m["max_abs_small"] <= MAX_ABS, m

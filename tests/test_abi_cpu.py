@@ -47,8 +47,8 @@ def test_status_strings(lib):
     assert lib.pfa_status_string(-999) == b"unknown status"
 
 
-def _fwd(lib, q=1, k=2, v=3, cu=4, num_seqs=1, max_seqlen=1, heads=1, head_dim=64, scale=1.0,
-         out=5, lse=6):
+def _fwd(lib, q=16, k=32, v=48, cu=64, num_seqs=1, max_seqlen=1, heads=1, head_dim=64, scale=1.0,
+         out=80, lse=96):
     return lib.pfa_varlen_fwd(q, k, v, cu, num_seqs, max_seqlen, heads, head_dim, scale, out, lse, None)
 
 
@@ -64,15 +64,23 @@ def test_argument_checks_run_before_any_hip_call(lib):
         assert _fwd(lib, head_dim=hd) == -5
     for sc in (0.0, -1.0, float("inf"), float("nan")):
         assert _fwd(lib, scale=sc) == -6
-    assert _fwd(lib, out=1) == -7
-    assert _fwd(lib, lse=2) == -7
-    assert _fwd(lib, lse=5) == -7
+    assert _fwd(lib, out=16) == -7
+    assert _fwd(lib, lse=32) == -7
+    assert _fwd(lib, lse=80) == -7
+    # q, k, v and out move in 16-byte vectors; lse and the table one element at a time
+    for name in ("q", "k", "v", "out"):
+        for off in (2, 8):
+            assert _fwd(lib, **{name: 256 + off}) == -12, (name, off)
+    assert _fwd(lib, lse=258) == -12
+    # a 4-byte aligned lse passes the alignment check (the size check after it fails)
+    assert _fwd(lib, lse=100, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
+    assert _fwd(lib, cu=66) == -12
     assert _fwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
     assert _fwd(lib, heads=2**17 + 1, head_dim=64) == -11     # a row over 2^23 elements
 
 
-def _fwd_qk(lib, q=1, k=2, v=3, cu_q=4, cu_k=8, num_seqs=1, max_q=1, max_k=1, heads=1,
-            head_dim=64, scale=1.0, out=5, lse=6):
+def _fwd_qk(lib, q=16, k=32, v=48, cu_q=64, cu_k=128, num_seqs=1, max_q=1, max_k=1, heads=1,
+            head_dim=64, scale=1.0, out=80, lse=96):
     return lib.pfa_varlen_fwd_qk(q, k, v, cu_q, cu_k, num_seqs, max_q, max_k, heads, head_dim, scale,
                                  out, lse, None)
 
@@ -86,9 +94,13 @@ def test_qk_argument_checks_run_before_any_hip_call(lib):
     assert _fwd_qk(lib, max_k=0) == -4
     assert _fwd_qk(lib, head_dim=96) == -5
     assert _fwd_qk(lib, scale=float("nan")) == -6
-    assert _fwd_qk(lib, out=8) == -7      # out aliases the key table
-    assert _fwd_qk(lib, lse=8) == -7
-    assert _fwd_qk(lib, lse=5) == -7
+    assert _fwd_qk(lib, out=128) == -7    # out aliases the key table
+    assert _fwd_qk(lib, lse=128) == -7
+    assert _fwd_qk(lib, lse=80) == -7
+    for name in ("q", "k", "v", "out"):
+        assert _fwd_qk(lib, **{name: 264}) == -12, name
+    assert _fwd_qk(lib, cu_k=130) == -12
+    assert _fwd_qk(lib, lse=97) == -12
     assert _fwd_qk(lib, num_seqs=2**30, heads=2**10, max_q=2**20) == -11
 
 
@@ -143,6 +155,10 @@ def test_blocksparse_argument_checks_run_before_any_hip_call(lib):
     assert _sparse(lib, out=96) == -7                        # out is the index array
     assert _sparse(lib, lse=80) == -7
     assert _sparse(lib, lse=112) == -7
+    for name in ("q", "k", "v", "out"):
+        assert _sparse(lib, **{name: 264}) == -12, name
+    for name in ("kv_ptr", "kv_idx", "lse", "cu"):
+        assert _sparse(lib, **{name: 258}) == -12, name
     assert _sparse(lib, max_seqlen=65537) == -11             # beyond the LDS list
     assert _sparse(lib, heads=2**17, head_dim=128) == -11
 
@@ -220,6 +236,10 @@ def test_fp8_argument_checks_run_before_any_hip_call(lib):
     assert _fp8(lib, out=48) == -7
     assert _fp8(lib, lse=64) == -7
     assert _fp8(lib, v8=56) == -12
+    for name in ("q", "k", "out"):
+        assert _fp8(lib, **{name: 264}) == -12, name
+    assert _fp8(lib, lse=258) == -12
+    assert _quant(lib, cu=34) == -12
     assert _fp8(lib, heads=2**17, head_dim=128) == -11
 
 
@@ -240,10 +260,14 @@ def test_fps_argument_checks_run_before_any_hip_call(lib):
     assert _fps(lib, out=112) == -7
     assert _fps(lib, lse=48) == -7
     assert _fps(lib, v_scale=68) == -12
+    for name in ("q", "k", "out"):
+        assert _fps(lib, **{name: 264}) == -12, name
+    for name in ("kv_ptr", "kv_idx", "lse", "cu"):
+        assert _fps(lib, **{name: 258}) == -12, name
     assert _fps(lib, max_seqlen=65537) == -11
 
 
-def _merge(lib, o_a=1, lse_a=2, o_b=3, lse_b=4, total=1, heads=1, head_dim=64, out=1, lse=2):
+def _merge(lib, o_a=16, lse_a=32, o_b=48, lse_b=64, total=1, heads=1, head_dim=64, out=16, lse=32):
     return lib.pfa_attn_merge(o_a, lse_a, o_b, lse_b, total, heads, head_dim, out, lse, None)
 
 
@@ -254,15 +278,19 @@ def test_merge_argument_checks_run_before_any_hip_call(lib):
     assert _merge(lib, total=-1) == -11
     assert _merge(lib, heads=0) == -3
     assert _merge(lib, head_dim=32) == -5
-    assert _merge(lib, out=2, lse=9) == -7     # out is an LSE input
-    assert _merge(lib, out=9, lse=1) == -7     # lse is an O input
-    assert _merge(lib, out=9, lse=9) == -7     # out and lse the same buffer
+    assert _merge(lib, out=32, lse=144) == -7    # out is an LSE input
+    assert _merge(lib, out=144, lse=16) == -7    # lse is an O input
+    assert _merge(lib, out=144, lse=144) == -7   # out and lse the same buffer
+    for name in ("o_a", "o_b", "out"):
+        assert _merge(lib, **{name: 264}) == -12, name
+    for name in ("lse_a", "lse_b", "lse"):
+        assert _merge(lib, **{name: 258}) == -12, name
     assert _merge(lib, total=0) == 0           # nothing to do, nothing launched
     assert _merge(lib, total=2**31, heads=1) == -11
 
 
-def _bwd(lib, q=1, k=2, v=3, out=4, dout=5, lse=6, cu=7, num_seqs=1, max_seqlen=1, heads=1,
-         head_dim=128, scale=1.0, dq=8, dk=9, dv=10, ws=11):
+def _bwd(lib, q=16, k=32, v=48, out=64, dout=80, lse=96, cu=112, num_seqs=1, max_seqlen=1, heads=1,
+         head_dim=128, scale=1.0, dq=128, dk=144, dv=160, ws=176):
     return lib.pfa_varlen_bwd(q, k, v, out, dout, lse, cu, num_seqs, max_seqlen, heads, head_dim,
                               scale, dq, dk, dv, ws, None)
 
@@ -275,10 +303,14 @@ def test_bwd_argument_checks_run_before_any_hip_call(lib):
     assert _bwd(lib, max_seqlen=0) == -4
     assert _bwd(lib, head_dim=32) == -5
     assert _bwd(lib, scale=0.0) == -6
-    assert _bwd(lib, dq=1) == -7          # output is an input
-    assert _bwd(lib, ws=6) == -7          # workspace is the LSE
-    assert _bwd(lib, dk=8) == -7          # two outputs share a buffer
-    assert _bwd(lib, ws=10) == -7
+    assert _bwd(lib, dq=16) == -7         # output is an input
+    assert _bwd(lib, ws=96) == -7         # workspace is the LSE
+    assert _bwd(lib, dk=128) == -7        # two outputs share a buffer
+    assert _bwd(lib, ws=160) == -7
+    for name in ("q", "k", "v", "out", "dout", "dq", "dk", "dv"):
+        assert _bwd(lib, **{name: 264}) == -12, name
+    for name in ("lse", "cu", "ws"):
+        assert _bwd(lib, **{name: 258}) == -12, name
     assert _bwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
 
 
