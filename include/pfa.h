@@ -329,6 +329,38 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
                            int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
                            void* dq, void* dk, void* dv, float* workspace, hipStream_t stream);
 
+/* Capacity, in fp32 values, of the device array that holds the row statistics of
+ * pfa_varlen_bwd_noalloc: 2 * heads * T of them must fit (heads * T <= 4,194,304). */
+#define PFA_BWD_SCRATCH_FLOATS (1 << 23)
+
+/*
+ * pfa_varlen_bwd_noalloc -- pfa_varlen_bwd for callers that cannot allocate device memory
+ * (code under graph capture, tight serving or training loops, harnesses that forbid
+ * allocation): the same gradients from the same three kernels, with the 2 * heads * T fp32
+ * row statistics kept in a library-held device array instead of a caller workspace.
+ *
+ * The array holds PFA_BWD_SCRATCH_FLOATS values (32 MiB), one copy per device the
+ * library runs on, allocated with the library's GPU code and held until the process ends.
+ * Its device address is looked up once per device, on the first call with that device
+ * current.  This call allocates and frees nothing.
+ *
+ * total_tokens  T = cu_seqlens[num_seqs], which the host cannot read without a copy; it
+ *               sizes the check 2 * heads * total_tokens <= PFA_BWD_SCRATCH_FLOATS
+ *               (PFA_ERR_SIZE otherwise).  If the table's last entry differs, the result is
+ *               undefined, but no access leaves the array: the kernels do nothing when the
+ *               table's T exceeds the array's capacity.
+ * Every other argument, the ownership rules and the errors are those of pfa_varlen_bwd.
+ *
+ * All calls on one device share that device's array and each call overwrites it, so two
+ * calls that overlap in time on one device (different streams, or several host threads)
+ * race and their results are undefined.  Calls on one stream are ordered and safe.
+ */
+PFA_API int pfa_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, const int32_t* cu_seqlens,
+                                   int num_seqs, int max_seqlen, int64_t total_tokens, int heads,
+                                   int head_dim, float scale, void* dq, void* dk, void* dv,
+                                   hipStream_t stream);
+
 /*
  * pfa_check_cu_seqlens -- host-side validator of a cu_seqlens table (no device calls).
  *

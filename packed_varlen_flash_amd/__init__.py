@@ -16,6 +16,7 @@ import numpy as np
 from . import _lib
 
 __all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv", "pfa_varlen_bwd",
+           "pfa_varlen_bwd_noalloc", "BWD_SCRATCH_FLOATS",
            "pfa_varlen_fwd_blocksparse", "block_layout_csr", "pfa_check_block_layout",
            "SPARSE_BLOCK_Q", "SPARSE_BLOCK_K", "pfa_quantize_v_fp8", "pfa_varlen_fwd_fp8pv",
            "pfa_varlen_fwd_blocksparse_fp8pv",
@@ -26,6 +27,7 @@ __all__ = ["pfa_varlen_fwd", "pfa_varlen_fwd_qk", "pfa_varlen_fwd_qkv", "pfa_var
 LIB_PATH = _lib.LIB_PATH
 SPARSE_BLOCK_Q = 256    # PFA_SPARSE_BLOCK_Q: query rows per block of a block-sparse layout
 SPARSE_BLOCK_K = 64     # PFA_SPARSE_BLOCK_K: keys per key block
+BWD_SCRATCH_FLOATS = 1 << 23   # PFA_BWD_SCRATCH_FLOATS: capacity of the backward's own array
 
 
 class PfaError(RuntimeError):
@@ -507,6 +509,46 @@ def pfa_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int,
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
         cu_seqlens.numel() - 1, int(max_seqlen), H, d, float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise PfaError(rc)
+    return dq, dk, dv
+
+
+def pfa_varlen_bwd_noalloc(q, k, v, out, dout, lse, cu_seqlens, max_seqlen: int, total_tokens: int,
+                           scale: float | None = None, dq=None, dk=None, dv=None, stream=None):
+    """pfa_varlen_bwd without a workspace: the row statistics live in the library's own
+    device array (see include/pfa.h), so with dq, dk and dv passed in nothing is allocated.
+    total_tokens must equal cu_seqlens[-1]; 2 * H * total_tokens must not exceed
+    BWD_SCRATCH_FLOATS.  Calls that overlap in time on one device race."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_bf16(name, t, torch)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have q's shape")
+    _check_table("cu_seqlens", cu_seqlens, torch)
+    T, H, d = q.shape
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout), ("cu_seqlens", cu_seqlens)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    if lse is None:
+        raise ValueError("lse must be the forward's contiguous fp32 [H, T]")
+    _check_buffer("lse", lse, q.device, torch.float32, (H, T))
+    if int(total_tokens) != T:
+        raise ValueError("total_tokens must be the packed token count (q.shape[0])")
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_buffer(name, t, q.device, torch.bfloat16, q.shape)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    rc = _lib.load().pfa_varlen_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, int(max_seqlen), int(total_tokens), H, d, float(scale), _ptr(dq),
+        _ptr(dk), _ptr(dv), ctypes.c_void_p(stream.cuda_stream))
     if rc != 0:
         raise PfaError(rc)
     return dq, dk, dv

@@ -38,6 +38,9 @@ _SIGNATURES = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "pfa_varlen_bwd": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 4 +
                        [ctypes.c_float] + [ctypes.c_void_p] * 5),
+    "pfa_varlen_bwd_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 2 +
+                               [ctypes.c_int64] + [ctypes.c_int] * 2 + [ctypes.c_float] +
+                               [ctypes.c_void_p] * 4),
     "pfa_check_cu_seqlens": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_void_p]),
     "pfa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

@@ -42,6 +42,7 @@ struct BwdParams {
   const __bf16* dout;
   const float* lse;
   float* ws;              // [2][heads][T]: -LSE*log2(e), then delta
+  int ws_rows;            // largest T the workspace holds: the kernels do nothing beyond it
   const int32_t* cu;
   __bf16* dq;
   __bf16* dk;
@@ -155,6 +156,7 @@ __device__ __forceinline__ void bwd_prep_row(const BwdParams& p, int T, int64_t 
 template <int D>
 __global__ void __launch_bounds__(256) pfa_bwd_prep_kernel(BwdParams p) {
   const int T = p.cu[p.num_seqs];   // T is known only on the device
+  if (T > p.ws_rows) return;
   for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < (int64_t)T * p.heads;
        row += (int64_t)gridDim.x * 256)
     bwd_prep_row<D>(p, T, row);
@@ -240,6 +242,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
   int* s_len = reinterpret_cast<int*>(qring);
 
   const int T = p.cu[p.num_seqs];
+  if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
                                                                    s_len, s_order, s_prefix)
@@ -405,6 +408,7 @@ pfa_bwd_dq_kernel(BwdParams p) {
   int* s_len = reinterpret_cast<int*>(kring);
 
   const int T = p.cu[p.num_seqs];
+  if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
                                                                    s_len, s_order, s_prefix)
@@ -548,18 +552,15 @@ pfa_bwd_dq_kernel(BwdParams p) {
 
 std::atomic<int> g_bwd_occ[kMaxDevices][2][2];   // [device][head_dim 64 / 128][dK-dV / dQ]
 
-}  // namespace
-
-extern "C" {
-
-PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
-                           const void* dout, const float* lse, const int32_t* cu_seqlens,
-                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
-                           void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
-  // ---- argument checks: all before any HIP runtime call
+// Argument checks shared by both backward entry points, all before any HIP runtime call.
+// workspace may be NULL only when the caller will not pass one (the allocation-free form).
+int check_bwd_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
+                   int head_dim, float scale, const void* dq, const void* dk, const void* dv,
+                   const float* workspace, bool workspace_required) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
       lse == nullptr || cu_seqlens == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
-      workspace == nullptr)
+      (workspace_required && workspace == nullptr))
     return PFA_ERR_NULL;
   if (num_seqs < 1) return PFA_ERR_NUM_SEQS;
   if (heads < 1) return PFA_ERR_HEADS;
@@ -568,10 +569,11 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
   if (!(std::isfinite(scale) && scale > 0.f)) return PFA_ERR_SCALE;
   const void* ins[7] = {q, k, v, out, dout, lse, cu_seqlens};
   const void* outs[4] = {dq, dk, dv, workspace};
-  for (int a = 0; a < 4; ++a) {
+  const int n_out = workspace != nullptr ? 4 : 3;
+  for (int a = 0; a < n_out; ++a) {
     for (const void* in : ins)
       if (in == outs[a]) return PFA_ERR_ALIAS;
-    for (int b = a + 1; b < 4; ++b)
+    for (int b = a + 1; b < n_out; ++b)
       if (outs[a] == outs[b]) return PFA_ERR_ALIAS;
   }
   // the [T, H, d] tensors move in 16-byte vectors; lse, workspace and the table element-wise
@@ -582,7 +584,16 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
   const int64_t tiles_max = ((int64_t)max_seqlen + kBwdRows - 1) / kBwdRows;
   const int64_t slots = (int64_t)num_seqs * heads * tiles_max;
   if ((int64_t)heads * head_dim > kMaxRowElems || slots > INT32_MAX) return PFA_ERR_SIZE;
+  return PFA_OK;
+}
 
+// The three backward launches, with the row statistics in ws (room for ws_rows tokens).
+int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+               const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
+               int head_dim, float scale, void* dq, void* dk, void* dv, float* ws, int ws_rows,
+               hipStream_t stream) {
+  const int64_t tiles_max = ((int64_t)max_seqlen + kBwdRows - 1) / kBwdRows;
+  const int64_t slots = (int64_t)num_seqs * heads * tiles_max;
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
   if (rc != PFA_OK) return rc;
@@ -623,7 +634,8 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
   bp.out = static_cast<const __bf16*>(out);
   bp.dout = static_cast<const __bf16*>(dout);
   bp.lse = lse;
-  bp.ws = workspace;
+  bp.ws = ws;
+  bp.ws_rows = ws_rows;
   bp.cu = cu_seqlens;
   bp.dq = static_cast<__bf16*>(dq);
   bp.dk = static_cast<__bf16*>(dk);
@@ -641,6 +653,62 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
   if (hipLaunchKernel(dqk, dim3(grid_for(occ_q)), dim3(threads), args, lds_dq, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   return PFA_OK;
+}
+
+// ---- allocation-free form: the row statistics live in a library-held device array.
+// One copy per device, allocated with the code object (it lives until the process ends).
+// In host code the array's name is only a stand-in for its device address; each device's
+// actual address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to a kernel.
+static __device__ __align__(256) float scratch[PFA_BWD_SCRATCH_FLOATS];
+std::atomic<float*> g_scratch[kMaxDevices];
+
+int scratch_for_current_device(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PFA_ERR_DEVICE;
+  float* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+      return PFA_ERR_DEVICE;
+    ptr = static_cast<float*>(addr);
+    g_scratch[dev].store(ptr, std::memory_order_release);   // a race stores the same address
+  }
+  *out = ptr;
+  return PFA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                           const void* dout, const float* lse, const int32_t* cu_seqlens,
+                           int num_seqs, int max_seqlen, int heads, int head_dim, float scale,
+                           void* dq, void* dk, void* dv, float* workspace, hipStream_t stream) {
+  const int rc = check_bwd_args(q, k, v, out, dout, lse, cu_seqlens, num_seqs, max_seqlen, heads, head_dim,
+                                scale, dq, dk, dv, workspace, true);
+  if (rc != PFA_OK) return rc;
+  return launch_bwd(q, k, v, out, dout, lse, cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale, dq, dk,
+                    dv, workspace, INT32_MAX, stream);
+}
+
+PFA_API int pfa_varlen_bwd_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                   const void* dout, const float* lse, const int32_t* cu_seqlens,
+                                   int num_seqs, int max_seqlen, int64_t total_tokens, int heads,
+                                   int head_dim, float scale, void* dq, void* dk, void* dv,
+                                   hipStream_t stream) {
+  int rc = check_bwd_args(q, k, v, out, dout, lse, cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale,
+                          dq, dk, dv, nullptr, false);
+  if (rc != PFA_OK) return rc;
+  // 2 * heads * T fp32 values of row statistics must fit the array
+  const int64_t ws_rows = (int64_t)PFA_BWD_SCRATCH_FLOATS / (2 * (int64_t)heads);
+  if (total_tokens < 0 || total_tokens > ws_rows) return PFA_ERR_SIZE;
+  float* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != PFA_OK) return rc;
+  return launch_bwd(q, k, v, out, dout, lse, cu_seqlens, num_seqs, max_seqlen, heads, head_dim, scale, dq, dk,
+                    dv, ws, (int)ws_rows, stream);
 }
 
 }  // extern "C"

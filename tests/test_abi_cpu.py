@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
                                        "pfa_varlen_fwd_blocksparse", "pfa_check_block_layout",
                                        "pfa_quantize_v_fp8", "pfa_varlen_fwd_fp8pv",
                                        "pfa_varlen_fwd_blocksparse_fp8pv",
-                                       "pfa_varlen_bwd", "pfa_attn_merge",
+                                       "pfa_varlen_bwd", "pfa_varlen_bwd_noalloc", "pfa_attn_merge",
                                        "pfa_check_cu_seqlens", "pfa_status_string"}
 
 
@@ -312,6 +312,27 @@ def test_bwd_argument_checks_run_before_any_hip_call(lib):
     for name in ("lse", "cu", "ws"):
         assert _bwd(lib, **{name: 258}) == -12, name
     assert _bwd(lib, num_seqs=2**30, heads=2**10, max_seqlen=2**20) == -11
+
+
+def _bwd_na(lib, q=16, k=32, v=48, out=64, dout=80, lse=96, cu=112, num_seqs=1, max_seqlen=1, T=1,
+            heads=1, head_dim=128, scale=1.0, dq=128, dk=144, dv=160):
+    return lib.pfa_varlen_bwd_noalloc(q, k, v, out, dout, lse, cu, num_seqs, max_seqlen, T, heads,
+                                      head_dim, scale, dq, dk, dv, None)
+
+
+def test_bwd_noalloc_argument_checks_run_before_any_hip_call(lib):
+    for name in ("q", "k", "v", "out", "dout", "lse", "cu", "dq", "dk", "dv"):
+        assert _bwd_na(lib, **{name: None}) == -1, name
+    assert _bwd_na(lib, num_seqs=0) == -2
+    assert _bwd_na(lib, heads=0) == -3
+    assert _bwd_na(lib, head_dim=96) == -5
+    assert _bwd_na(lib, dq=16) == -7
+    assert _bwd_na(lib, dk=128) == -7
+    assert _bwd_na(lib, dv=264) == -12
+    # 2 * heads * T must fit the library's 2^23-value array
+    assert _bwd_na(lib, T=-1) == -11
+    assert _bwd_na(lib, heads=8, T=2**19 + 1) == -11
+    assert _bwd_na(lib, heads=1, T=2**22 + 1) == -11
 
 
 def test_host_validator(lib):
