@@ -114,7 +114,12 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
  * cu_seqlens_q, cu_seqlens_k   device int32 [num_seqs + 1]; passing the same pointer for
  *               both selects the self-attention kernel.
  * max_seqlen_q  bound on every query segment length (>= 1); sizes the launch.
- * max_seqlen_k  bound on every key segment length (>= 1); not used by the kernel.
+ * max_seqlen_k  bound on every key segment length (>= 1).  At most 256 (head_dim 128) or
+ *               128 (head_dim 64) selects a kernel that holds each (segment, head)'s K and V
+ *               in LDS for all of its query tiles; above it K/V stream in 64-key stages.
+ *               Both give bitwise equal results.  A key segment longer than this bound
+ *               breaks the precondition below: the resident kernel then reads only its
+ *               first 256 (128) keys, and still reads and writes no row out of range.
  * lse           fp32 [heads, Tq] or NULL.
  * Everything else, ownership and errors as for pfa_varlen_fwd.  A segment with queries
  * but no keys has no softmax; its rows get O = 0 and LSE = -inf.  Both tables must

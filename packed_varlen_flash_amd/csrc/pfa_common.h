@@ -33,6 +33,17 @@ constexpr int kStages = 2;       // LDS ring depth (stages)
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
 constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
 constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
+// s_waitcnt vmcnt(n), other counters unconstrained (vmcnt bits 3:0 and 15:14)
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// a pointer the caller knows to be wave-uniform, in scalar registers (a buffer resource
+// built from it then needs no per-lane loop)
+__device__ __forceinline__ void* uniform_ptr(const void* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

@@ -760,6 +760,342 @@ pfa_fwd_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------------
+// Cross-attention over short key segments, with each key segment's K and V resident in
+// LDS for all of its query tiles.
+//
+// The xxmr.cn editing-network article (section 4.1) describes cross-attention whose keys
+// and values come from a condition or edit sequence much shorter than the image-token
+// query sequence.  With a key segment of a few hundred tokens, the streaming kernel above
+// reloads all of it for every 256-query tile and spends most of each tile starting up.
+// Here a workgroup takes a contiguous run of the longest-first item list, loads the key
+// segment's K and V once per (segment, head) it meets, keeps them in LDS, and streams
+// only Q in and O out: no stage loads and no stage barriers inside a tile.  The stage
+// routine is the streaming kernel's own.
+// ---------------------------------------------------------------------------------
+// Longest key segment held in LDS: K and V of 256 keys at d = 128 (128 KiB) or 128 keys
+// at d = 64 (32 KiB, so two workgroups still share a CU).
+template <int D>
+constexpr int resident_keys() { return D == 128 ? 256 : 128; }
+
+template <int D, int QB, int NW>
+struct ResidentTile {
+  using C = Tile<D, QB, NW, 64>;
+  static constexpr int KMAX = resident_keys<D>();
+  static constexpr int NSMAX = KMAX / 64;                 // resident 64-key stages
+  static constexpr int KV_BYTES = KMAX * D * 2;           // K area; the V area follows
+  static constexpr int OUT_ROWS = QB * 32;                // one wave's query rows
+  static constexpr int STAGE_OUT = NW * OUT_ROWS * 64;    // output staging: 32 channels a time
+  static constexpr int CU_INTS = 2 * (kSortMax + 1);       // cu_seqlens_q and _k, sorted mode
+  // vector-memory instructions of one tile's epilogue: the output stores, then one LSE
+  // store per query block (all issued, rows past the segment end dropped by the buffer
+  // bounds)
+  static constexpr int EPI_STORES = C::DT * (OUT_ROWS * 4 / kWave) + QB;
+  static constexpr size_t LDS_BYTES =
+      (size_t)2 * KV_BYTES + STAGE_OUT + sizeof(int) * (C::SCHED_INTS + CU_INTS);
+  static_assert(sizeof(int) * kSortMax <= (size_t)KV_BYTES, "len scratch fits the K area");
+  static_assert(EPI_STORES < 64, "fits the vmcnt field");
+};
+
+// Stages [i0, i1) of one key segment's K and V, global -> LDS (stage i at offset
+// i * TILE_BYTES of each area, in the streaming kernel's stage layout), bounded at the
+// segment end.  (A device function: the HIP host pass does not instantiate a kernel
+// template that calls the buffer-to-LDS load builtin itself.)
+template <int D, int QB, int NW>
+__device__ __forceinline__ void resident_load(const __bf16* kbase, const __bf16* vbase, int Lk, int i0, int i1,
+                                              int64_t rs, char* kres, char* vres, int wave,
+                                              const int (&src_k)[Tile<D, QB, NW, 64>::CPT],
+                                              const int (&src_v)[Tile<D, QB, NW, 64>::CPT]) {
+  using C = Tile<D, QB, NW, 64>;
+  const int kbytes = (int)(rs * 2);
+  for (int i = i0; i < i1; ++i) {
+    const int rows = (Lk - 64 * i < 64) ? (Lk - 64 * i) : 64;
+    __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)64 * i * rs), 0, rows * kbytes, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)64 * i * rs), 0, rows * kbytes, kRsrcFlags);
+    char* kd = kres + i * C::TILE_BYTES + wave * C::CPT * 1024;
+    char* vd = vres + i * C::TILE_BYTES + wave * C::CPT * 1024;
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kd + j * 1024), 16, src_k[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vd + j * 1024), 16, src_v[j], 0, 0, 0);
+    }
+  }
+}
+
+template <int D, int QB, int NW, int WPE>
+__global__ void __launch_bounds__(kWave * NW) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+pfa_fwd_resident_kernel(Params p) {
+  using R = ResidentTile<D, QB, NW>;
+  using C = typename R::C;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  char* const kres = reinterpret_cast<char*>(smem);
+  char* const vres = kres + R::KV_BYTES;
+  char* const ostg = vres + R::KV_BYTES;
+  int* s_order = reinterpret_cast<int*>(ostg + R::STAGE_OUT);
+  int* s_prefix = s_order + kSortMax;
+  int* s_cuq = s_order + C::SCHED_INTS;        // sorted mode: cu_seqlens_q, then _k
+  int* s_cuk = s_cuq + kSortMax + 1;
+  int* s_len = reinterpret_cast<int*>(kres);   // scratch, dead before the first K/V load
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31;
+  const int g = lane >> 5;
+  const int i16 = lane & 15;
+  const int hh = (lane >> 4) & 1;
+  const int64_t rs = (int64_t)p.heads * D;
+  const int kbytes = (int)(rs * 2);
+  const float c = p.c;
+
+  const int Tq = p.cu_q[p.num_seqs];
+  const int Tk = p.cu_k[p.num_seqs];
+  const bool sorted = p.num_seqs <= kSortMax;
+  // Item decoding reads the segment tables from LDS (sorted mode), so that no vector-memory
+  // load sits between the next tile's Q loads and the wait for them.
+  if (sorted)
+    for (int i = tid; i <= p.num_seqs; i += C::THREADS) {
+      s_cuq[i] = p.cu_q[i];
+      s_cuk[i] = p.cu_k[i];
+    }
+  const int total = sorted ? build_schedule<C::BM, C::THREADS>(p.cu_q, p.cu_k, p.num_seqs, p.heads, s_len,
+                                                               s_order, s_prefix)
+                           : p.num_seqs * p.heads * p.qt_max;
+  // a contiguous run of the item list per workgroup: consecutive items share a
+  // (segment, head) and its resident K/V
+  const int64_t u_begin = (int64_t)total * blockIdx.x / gridDim.x;
+  const int64_t u_end = (int64_t)total * (blockIdx.x + 1) / gridDim.x;
+
+  // per-lane offsets: K rows (A operand of S^T), transposed V reads, stage-load sources
+  int koff[C::KSTEP], voff[C::DT];
+#pragma unroll
+  for (int t = 0; t < C::KSTEP; ++t) koff[t] = phys_off<D, Swz::K>(n32, 2 * t + g);
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+    voff[dt] = phys_off<D, Swz::V>(4 * g + (i16 >> 2), 4 * dt + 2 * hh + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
+  int src_k[C::CPT], src_v[C::CPT];
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int P = (wave * C::CPT + i) * 64 + lane;
+    src_k[i] = logical_src<D, Swz::K>(P, kbytes);
+    src_v[i] = logical_src<D, Swz::V>(P, kbytes);
+  }
+
+  // work item u -> (segment, head, query tile) and the tile's query rows (all fields
+  // wave-uniform; rank and nt: sorted mode only)
+  struct Item {
+    int s, h, qt, qa, Lq, rank, nt;
+  };
+  auto rfl = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  // false if the tile holds no query rows
+  auto rows_of = [&](Item& it, int qe) -> bool {
+    it.Lq = qe - it.qa;
+    if (it.qa < 0 || it.qa >= Tq) return false;
+    if (it.Lq > Tq - it.qa) it.Lq = Tq - it.qa;
+    return it.Lq > 0 && it.qt * C::BM < it.Lq;
+  };
+  auto decode = [&](int64_t u, Item& it) -> bool {
+    int qe;
+    if (sorted) {
+      int lo = 0, hi = p.num_seqs - 1;   // last rank r with s_prefix[r] <= u
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (rfl(s_prefix[mid]) <= u) lo = mid; else hi = mid - 1;
+      }
+      it.rank = lo;
+      it.s = rfl(s_order[lo]);
+      it.qa = rfl(s_cuq[it.s]);
+      qe = rfl(s_cuq[it.s + 1]);
+      it.nt = (qe - it.qa + C::BM - 1) / C::BM;   // >= 1: a rank that holds item u has items
+      const int local = (int)u - rfl(s_prefix[lo]);
+      it.h = local / it.nt;
+      it.qt = local - it.h * it.nt;
+    } else {
+      const int per_seg = p.heads * p.qt_max;
+      it.s = (int)u / per_seg;
+      const int rem = (int)u - it.s * per_seg;
+      it.h = rem / p.qt_max;
+      it.qt = rem - it.h * p.qt_max;
+      it.qa = rfl(p.cu_q[it.s]);
+      qe = rfl(p.cu_q[it.s + 1]);
+    }
+    return rows_of(it, qe);
+  };
+  // it holds item u - 1 (sorted mode: as decode left it); step it to item u.  Sorted mode
+  // walks the list (next query tile, then head, then rank) instead of searching it.
+  auto advance = [&](int64_t u, Item& it) -> bool {
+    if (!sorted) return decode(u, it);
+    if (++it.qt >= it.nt) {
+      it.qt = 0;
+      if (++it.h >= p.heads) {
+        it.h = 0;
+        while (it.rank + 1 < p.num_seqs && rfl(s_prefix[it.rank + 1]) <= u) ++it.rank;
+        it.s = rfl(s_order[it.rank]);
+        it.qa = rfl(s_cuq[it.s]);
+        it.nt = (rfl(s_cuq[it.s + 1]) - it.qa + C::BM - 1) / C::BM;
+      }
+    }
+    return rows_of(it, rfl(s_cuq[it.s + 1]));
+  };
+  // Q fragments of an item's tile (rows past the segment end are zero)
+  auto load_q = [&](const Item& it, bf16x8 (&dst)[QB][C::KSTEP]) {
+    const __bf16* qbase = p.q + (int64_t)it.qa * rs + (int64_t)it.h * D;
+    const int q0 = it.qt * C::BM + wave * (QB * 32);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const int row = q0 + b * 32 + n32;
+#pragma unroll
+      for (int t = 0; t < C::KSTEP; ++t) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row < it.Lq) x = *reinterpret_cast<const u32x4*>(qbase + (int64_t)row * rs + 16 * t + 8 * g);
+        dst[b][t] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+  };
+
+  // At d = 128 the next item's Q is loaded while the current tile computes, and before
+  // its output stores: waiting for it then waits for no store.  (At d = 64 the second Q
+  // register set does not fit beside two query blocks.)
+  constexpr bool kPrefetchQ = D == 128;
+  int64_t u = u_begin;
+  Item cur;
+  bool have = false;
+  while (u < u_end && !(have = decode(u, cur))) ++u;
+  bf16x8 qn[QB][C::KSTEP];
+  if (kPrefetchQ && have) load_q(cur, qn);
+  // nothing is in flight at the loop head but what the loop itself issued: without this
+  // wait the compiler guards the stage loop's first products with a full vmcnt wait (it
+  // cannot tell which path reaches them), and that wait would take in the next tile's Q
+  __builtin_amdgcn_s_waitcnt(kWaitVmem);
+  // first row and length of segment s's keys, clamped to the table and to the LDS bound (a
+  // longer segment breaks the caller's max_seqlen_k; the kernel still stays in LDS)
+  auto key_span = [&](int s_, int& ka, int& len) {
+    if (sorted) {
+      ka = rfl(s_cuk[s_]);
+      len = rfl(s_cuk[s_ + 1]) - ka;
+    } else {
+      ka = rfl(p.cu_k[s_]);
+      len = rfl(p.cu_k[s_ + 1]) - ka;
+      // keeps the two branches' loads apart: merged, they become one generic-address load
+      // whose wait would take in the next tile's Q loads
+      asm volatile("" ::: "memory");
+    }
+    if (ka < 0 || ka > Tk) ka = Tk;
+    if (len > Tk - ka) len = Tk - ka;
+    if (len < 0) len = 0;
+    if (len > R::KMAX) len = R::KMAX;
+  };
+  int res_s = -1, res_h = -1, ns = 0, Lk = 0;
+  while (have) {
+    const int s = cur.s, h = cur.h, qt = cur.qt, qa = cur.qa, Lq = cur.Lq;
+    if (s != res_s || h != res_h) {
+      // a new (segment, head): every wave is done with the old K/V, then all of the key
+      // segment's stages come in global -> LDS, bounded at its end
+      __syncthreads();
+      int ka;
+      key_span(s, ka, Lk);
+      ns = (Lk + 63) / 64;
+      resident_load<D, QB, NW>(p.k + (int64_t)ka * rs + (int64_t)h * D, p.v + (int64_t)ka * rs + (int64_t)h * D,
+                               Lk, 0, ns, rs, kres, vres, wave, src_k, src_v);
+      __builtin_amdgcn_s_waitcnt(kWaitVmem);
+      __syncthreads();
+      res_s = s;
+      res_h = h;
+    }
+
+    // ---- one query tile against the resident stages
+    const int64_t head_off = (int64_t)h * D;
+    const int q0 = qt * C::BM + wave * (QB * 32);
+    TileState<D, QB> st;
+    if constexpr (kPrefetchQ)
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(R::EPI_STORES));   // the Q loads, not the stores after them
+    else
+      load_q(cur, qn);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+#pragma unroll
+      for (int t = 0; t < C::KSTEP; ++t) st.qr[b][t] = qn[b][t];
+      st.m_run[b] = -INFINITY;
+      st.l_run[b] = 0.f;
+      st.l_rnd[b] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.o[b][dt][i] = 0.f;
+    }
+    Item nxt;
+    bool have_next = false;
+    int64_t un = u + 1;
+    if (un < u_end) {
+      nxt = cur;
+      while (!(have_next = advance(un, nxt)) && ++un < u_end) {}
+    }
+    if (kPrefetchQ && have_next) load_q(nxt, qn);
+    auto no_issue = [](char*, char*, int) {};
+#pragma unroll 1
+    for (int i = 0; i < ns; ++i)
+      stage_body<D, QB, 64>(st, nullptr, nullptr, kres + i * C::TILE_BYTES, vres + i * C::TILE_BYTES, false,
+                            no_issue, i, 64 * i, Lk, koff, voff, c, g);
+
+    // ---- epilogue: O = acc / l_rnd in bf16, LSE; O leaves 32 channels at a time through
+    // the wave's part of the staging area (rows of 64 bytes, 16-byte chunks XORed with
+    // bits 2-3 of the row), read back as whole 64-byte row pieces
+    // Every store is issued; the buffer bounds (this wave's valid rows) drop the rest, so
+    // the count of vector-memory instructions after the next tile's Q loads is fixed.
+    char* const ost = ostg + wave * (R::OUT_ROWS * 64);
+    int vrows = Lq - q0;
+    vrows = vrows < 0 ? 0 : (vrows > R::OUT_ROWS ? R::OUT_ROWS : vrows);
+    vrows = __builtin_amdgcn_readfirstlane(vrows);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(p.out + (int64_t)(qa + q0) * rs + head_off), 0, vrows * kbytes, kRsrcFlags);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        p.lse != nullptr ? uniform_ptr(p.lse + (int64_t)h * Tq + qa + q0) : nullptr, 0,
+        p.lse != nullptr ? vrows * 4 : 0, kRsrcFlags);
+    float inv[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const float lt = partner_sum(st.l_run[b]);
+      const float lr = partner_sum(st.l_rnd[b]);
+      inv[b] = lr > 0.f ? 1.0f / lr : 0.f;   // no keys: O = 0 (and LSE = -inf)
+      const int r = b * 32 + n32;
+      const float lse_r = (st.m_run[b] + __builtin_amdgcn_logf(lt)) * kLn2;
+      // the second half-wave holds the same rows: its offset lies past every bound
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_r), rl,
+                                            g == 0 ? 4 * r : 0x40000000, 0, 0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b) {
+        const int r = b * 32 + n32;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(st.o[b][dt][4 * ii + e] * inv[b]);
+          *reinterpret_cast<bf16x4*>(ost + r * 64 + ((ii ^ ((r >> 2) & 3)) << 4) + 8 * g) = w;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave reads back what it wrote
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < R::OUT_ROWS * 4 / kWave; ++k) {
+        const int P = k * kWave + lane;
+        const int r = P >> 2, ch = P & 3;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(ost + r * 64 + ((ch ^ ((r >> 2) & 3)) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(x, ro, r * kbytes + 64 * dt + 16 * ch, 0, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // reads done before the next tile of channels
+      __builtin_amdgcn_wave_barrier();
+    }
+    cur = nxt;
+    u = un;
+    have = have_next;
+  }
+}
+
+// ---------------------------------------------------------------------------------
 // Key rotation pass of the fused-projection forward: k_rot[t, h, :] = RoPE(k[t, h, :])
 // with token t's angles, written contiguous [T, heads, D].  The forward kernel re-reads
 // every key stage once per query tile of its segment, so the keys are rotated once here
@@ -821,10 +1157,19 @@ Variant make_variant() {
                  C::THREADS, C::LDS_BYTES + (mode_sparse(MODE) ? kSparseLdsBytes : 0)};
 }
 
-constexpr int kVariants = 12;  // head_dim 64, 128 x the six kernel modes
+// head_dim 64, 128 x (the six kernel modes, the resident-K/V cross kernel)
+constexpr int kModeResident = 6;
+constexpr int kVariants = 14;
 std::atomic<int> g_occ[kMaxDevices][kVariants];
 
 int variant_index(int head_dim, int mode) { return (head_dim == 64 ? 0 : 1) + 2 * mode; }
+
+template <int D, int QB, int NW, int WPE>
+Variant make_resident_variant() {
+  using R = ResidentTile<D, QB, NW>;
+  return Variant{reinterpret_cast<const void*>(&pfa_fwd_resident_kernel<D, QB, NW, WPE>), R::C::BM,
+                 R::C::THREADS, R::LDS_BYTES};
+}
 
 #ifndef PFA_D64_QB
 #define PFA_D64_QB 2
@@ -858,6 +1203,9 @@ Variant variant_of(int head_dim) {
 }
 
 Variant variant_for(int head_dim, int mode) {
+  if (mode == kModeResident)
+    return head_dim == 64 ? make_resident_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_WPE>()
+                          : make_resident_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_WPE>();
   return mode == kModeCross  ? variant_of<kModeCross>(head_dim)
        : mode == kModeQkv    ? variant_of<kModeQkv>(head_dim)
        : mode == kModeSparse ? variant_of<kModeSparse>(head_dim)
@@ -968,7 +1316,11 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const
   prm.num_seqs = num_seqs;
   prm.heads = heads;
   prm.c = scale * kLog2e;
-  const int mode = cu_seqlens_k != cu_seqlens_q ? kModeCross : kModeSelf;
+  // separate tables whose key segments all fit in LDS: the resident-K/V kernel
+  const int resident_max = head_dim == 64 ? resident_keys<64>() : resident_keys<128>();
+  const int mode = cu_seqlens_k == cu_seqlens_q ? kModeSelf
+                 : max_seqlen_k <= resident_max  ? kModeResident
+                                                 : kModeCross;
   return launch_fwd(prm, mode, max_seqlen_q, head_dim, stream);
 }
 

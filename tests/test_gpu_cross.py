@@ -184,3 +184,60 @@ def test_poison_in_other_segments_does_not_leak():
     ob2, lse2 = _run(y, "poisoned neighbours")
     np.testing.assert_array_equal(ob2[qa:qb], ob[qa:qb])
     np.testing.assert_array_equal(lse2[:, qa:qb], lse[:, qa:qb])
+
+
+# ---- short key segments: the resident-K/V kernel (every key segment held in LDS for all
+# of its query tiles; chosen when max_seqlen_k <= 256 at d = 128, <= 128 at d = 64)
+
+def _short_keys(seed, d, kmax):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(2, 7))
+    lq = [int(x) for x in rng.integers(1, 1800, size=n)]
+    lk = W.random_lengths(rng, n, kmax)
+    return W.make_cross(lq, lk, 3, d, seed=seed, name=f"shortk{seed}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_resident_kv_random_packs_full(seed):
+    d = 64 if seed % 2 else 128
+    x = _short_keys(500 + seed, d, 128 if d == 64 else 256)   # max_k = longest key segment
+    _check(x, f"resident K/V seed={seed} d={d} Lq={x.lengths_q} Lk={x.lengths_k}")
+
+
+def test_resident_kv_matches_the_streaming_kernel_bitwise():
+    """The same data through both kernels (a key bound above the resident limit selects
+    the streaming one): same stages in the same order, so bitwise equal."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd_qk
+    for d, kmax in ((128, 256), (64, 128)):
+        x = W.make_cross([4096, 1, 300, 1024, 700, 0], [256, 1, 64, 0, 200, 5] if d == 128 else
+                         [128, 1, 64, 0, 100, 5], 4, d, seed=600 + d, name="resident-vs-stream")
+        q, k, v, cq, ck = _upload(x)
+        o1, l1 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax, x.scale)        # resident
+        o2, l2 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax + 1, x.scale)    # streaming
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), d
+        assert torch.equal(l1, l2), d
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_resident_kv_switching_matches_the_streaming_kernel_bitwise(d):
+    """More tiles than workgroups, so each workgroup runs several (segment, head) key sets in
+    a row and loads the next one into the slots of the last tile as it frees them: key
+    stage counts rising, falling, and an empty key segment between them."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd_qk
+    kmax = 256 if d == 128 else 128
+    lk = [256, 0, 64, 200, 1, 130] if d == 128 else [128, 0, 64, 100, 1, 65]
+    heads = 32 if d == 128 else 48
+    x = W.make_cross([2048, 1500, 700, 3000, 1, 900], lk, heads, d, seed=700 + d, name="resident-switch")
+    q, k, v, cq, ck = _upload(x)
+    say(f"[gpu] resident K/V switching d={d} H={heads} Lk={lk}")
+    o1, l1 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax, x.scale)        # resident
+    o2, l2 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax + 1, x.scale)    # streaming
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), d
+    assert torch.equal(l1, l2), d
+    # and the resident kernel against the oracle on sampled rows of every segment
+    rows = W.sample_rows(x.cu_q, stride=97, edge=8, full_upto=0)
+    _check(x, f"resident-switch d={d} sampled {len(rows)} rows", rows=rows)
