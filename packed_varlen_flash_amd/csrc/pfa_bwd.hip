@@ -245,7 +245,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
-                                                                   s_len, s_order, s_prefix)
+                                                                   s_len, s_order, s_prefix, kSortMax)
                            : p.num_seqs * p.heads * p.tiles_max;
   const int G = gridDim.x;
   const int bid = blockIdx.x;
@@ -411,7 +411,7 @@ pfa_bwd_dq_kernel(BwdParams p) {
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
-                                                                   s_len, s_order, s_prefix)
+                                                                   s_len, s_order, s_prefix, kSortMax)
                            : p.num_seqs * p.heads * p.tiles_max;
   const int G = gridDim.x;
   const int bid = blockIdx.x;

@@ -31,7 +31,8 @@ constexpr int kWave = 64;
 constexpr int kHalf = 64;        // keys per softmax step (two 32-key sub-blocks)
 constexpr int kStages = 2;       // LDS ring depth (stages)
 constexpr int kRsrcFlags = 0x00020000;  // raw buffer resource word 3 (32-bit data format)
-constexpr int kSortMax = 512;    // segment tables up to this size are sorted on device
+constexpr int kSortMax = 512;    // schedule capacity every kernel's LDS holds
+constexpr int kSortCapMax = 4096;   // largest table the streaming forward sorts (more LDS)
 constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters unconstrained
 // s_waitcnt vmcnt(n), other counters unconstrained (vmcnt bits 3:0 and 15:14)
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
@@ -91,30 +92,69 @@ __device__ __forceinline__ int logical_src(int P, int row_bytes) {
 // ---------------------------------------------------------------------------------
 // Device-side scheduler: decode cu_seqlens into a longest-first list of work items.
 // ---------------------------------------------------------------------------------
-// Sorted mode (num_seqs <= kSortMax): s_order[r] = segment of rank r (key length, i.e.
-// the work per query tile, descending; ties by index), s_prefix[r] = first item of rank
-// r; a segment has heads * ceil(query length / BM) items, ordered head-major,
-// query-tile-minor.  Returns the item count.
+// Sorted mode (num_seqs <= the kernel's schedule capacity cap): s_order[r] = segment of
+// rank r (key length, i.e. the work per query tile, descending; ties by index), s_prefix[r]
+// = first item of rank r; a segment has heads * ceil(query length / BM) items, ordered
+// head-major, query-tile-minor.  Returns the item count.  s_order holds cap entries,
+// s_prefix n + 1; scratch (dead LDS of the caller's tile area) at least max(n, THREADS)
+// ints.  Up to kSortMax segments each thread ranks its segments by counting; above, a
+// bitonic sort of (length, index) keys over cap (a power of two) entries.
+constexpr int kSortIdxBits = 13;                          // segment index in a sort key
+constexpr int kSortLenMax = (1 << (32 - kSortIdxBits)) - 1;   // longer keys tie (index order)
+// every real key stays below the padding key 0xFFFFFFFF
+static_assert((1 << kSortIdxBits) > kSortCapMax, "index field holds every segment, with room");
+
 template <int BM, int THREADS>
 __device__ int build_schedule(const int32_t* cu_q, const int32_t* cu_k, int n, int heads,
-                              int* s_len, int* s_order, int* s_prefix) {
+                              int* scratch, int* s_order, int* s_prefix, int cap) {
   const int tid = threadIdx.x;
-  for (int s = tid; s < n; s += THREADS) {
-    int L = cu_k[s + 1] - cu_k[s];
-    s_len[s] = L > 0 ? L : 0;
-  }
-  __syncthreads();
-  for (int s = tid; s < n; s += THREADS) {
-    const int L = s_len[s];
-    int rank = 0;
-    for (int t = 0; t < n; ++t) {
-      const int Lt = s_len[t];
-      rank += (Lt > L) || (Lt == L && t < s);
+  if (n <= kSortMax) {
+    int* s_len = scratch;
+    for (int s = tid; s < n; s += THREADS) {
+      int L = cu_k[s + 1] - cu_k[s];
+      s_len[s] = L > 0 ? L : 0;
     }
-    s_order[rank] = s;
+    __syncthreads();
+    for (int s = tid; s < n; s += THREADS) {
+      const int L = s_len[s];
+      int rank = 0;
+      for (int t = 0; t < n; ++t) {
+        const int Lt = s_len[t];
+        rank += (Lt > L) || (Lt == L && t < s);
+      }
+      s_order[rank] = s;
+    }
+  } else {
+    // ascending keys = descending length, then ascending index; padding sorts last
+    uint32_t* key = reinterpret_cast<uint32_t*>(s_order);
+    for (int i = tid; i < cap; i += THREADS) {
+      uint32_t kv = 0xFFFFFFFFu;
+      if (i < n) {
+        int L = cu_k[i + 1] - cu_k[i];
+        L = L < 0 ? 0 : (L > kSortLenMax ? kSortLenMax : L);
+        kv = ((uint32_t)(kSortLenMax - L) << kSortIdxBits) | (uint32_t)i;
+      }
+      key[i] = kv;
+    }
+    __syncthreads();
+    for (int k = 2; k <= cap; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int t = tid; t < (cap >> 1); t += THREADS) {
+          const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1));   // lower element of the pair
+          const uint32_t a = key[i], b = key[i + j];
+          if ((a > b) == ((i & k) == 0)) {
+            key[i] = b;
+            key[i + j] = a;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int r = tid; r < n; r += THREADS) s_order[r] = (int)(key[r] & ((1u << kSortIdxBits) - 1));
   }
   __syncthreads();
-  // items per rank, then an inclusive Hillis-Steele scan in place (n <= kSortMax)
+  // items per rank, then an inclusive scan: each thread runs over its own chunk of ranks,
+  // a Hillis-Steele scan over the chunk totals, and the chunk offsets are added back
   for (int r = tid; r < n; r += THREADS) {
     const int sg = s_order[r];
     int Lq = cu_q[sg + 1] - cu_q[sg];
@@ -123,21 +163,26 @@ __device__ int build_schedule(const int32_t* cu_q, const int32_t* cu_k, int n, i
   }
   if (tid == 0) s_prefix[0] = 0;
   __syncthreads();
-  for (int off = 1; off < n; off <<= 1) {
-    int add[kSortMax / THREADS];
-#pragma unroll
-    for (int j = 0; j < kSortMax / THREADS; ++j) {
-      const int r = tid + j * THREADS;
-      add[j] = (r < n && r >= off) ? s_prefix[r + 1 - off] : 0;
-    }
+  const int per = (n + THREADS - 1) / THREADS;
+  const int chunks = (n + per - 1) / per;
+  const int r0 = tid * per;
+  const int r1 = r0 + per < n ? r0 + per : n;
+  int run = 0;
+  for (int r = r0; r < r1; ++r) {
+    run += s_prefix[r + 1];
+    s_prefix[r + 1] = run;
+  }
+  if (tid < chunks) scratch[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < chunks; off <<= 1) {
+    const int add = (tid < chunks && tid >= off) ? scratch[tid - off] : 0;
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSortMax / THREADS; ++j) {
-      const int r = tid + j * THREADS;
-      if (r < n) s_prefix[r + 1] += add[j];
-    }
+    if (tid < chunks) scratch[tid] += add;
     __syncthreads();
   }
+  const int before = (tid > 0 && tid < chunks) ? scratch[tid - 1] : 0;
+  for (int r = r0; r < r1; ++r) s_prefix[r + 1] += before;
+  __syncthreads();
   return s_prefix[n];
 }
 

@@ -54,6 +54,7 @@ struct Params {
   int num_seqs;
   int heads;
   int qt_max;      // ceil(max_seqlen / BM): slots per (segment, head) in unsorted mode
+  int sort_cap;    // schedule capacity held in LDS (tables up to it are sorted)
   float c;         // scale * log2(e)
   // fused-projection variant only: row strides (elements) of q, k, v, and the rotary
   // angle tables [T, D/2] applied to q as it is loaded (nullptr: no rotation)
@@ -698,17 +699,17 @@ pfa_fwd_kernel(Params p) {
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
   __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
   int* s_order = reinterpret_cast<int*>(smem + 2 * kStages * C::TILE_BYTES);
-  int* s_prefix = s_order + kSortMax;
-  int* s_blk = s_order + C::SCHED_INTS;     // block-sparse variant only (its LDS is larger)
-  int* s_len = reinterpret_cast<int*>(ks);  // scratch, dead before the first K tile lands
+  int* s_prefix = s_order + p.sort_cap;
+  int* s_blk = s_order + 2 * p.sort_cap + 8;   // block-sparse variant only (its LDS is larger)
+  int* s_len = reinterpret_cast<int*>(ks);     // scratch, dead before the first K tile lands
 
   const int Tq = p.cu_q[p.num_seqs];
   const int Tk = cu_k[p.num_seqs];
-  const bool sorted = p.num_seqs <= kSortMax;
+  const bool sorted = p.num_seqs <= p.sort_cap;
   int total;
   if (sorted) {
     total = build_schedule<C::BM, C::THREADS>(p.cu_q, cu_k, p.num_seqs, p.heads, s_len, s_order,
-                                              s_prefix);
+                                              s_prefix, p.sort_cap);
   } else {
     total = p.num_seqs * p.heads * p.qt_max;
   }
@@ -860,7 +861,7 @@ pfa_fwd_resident_kernel(Params p) {
       s_cuk[i] = p.cu_k[i];
     }
   const int total = sorted ? build_schedule<C::BM, C::THREADS>(p.cu_q, p.cu_k, p.num_seqs, p.heads, s_len,
-                                                               s_order, s_prefix)
+                                                               s_order, s_prefix, kSortMax)
                            : p.num_seqs * p.heads * p.qt_max;
   // a contiguous run of the item list per workgroup: consecutive items share a
   // (segment, head) and its resident K/V
@@ -1160,7 +1161,8 @@ Variant make_variant() {
 // head_dim 64, 128 x (the six kernel modes, the resident-K/V cross kernel)
 constexpr int kModeResident = 6;
 constexpr int kVariants = 14;
-std::atomic<int> g_occ[kMaxDevices][kVariants];
+constexpr int kSortClasses = 4;   // schedule capacities 512, 1024, 2048, 4096
+std::atomic<int> g_occ[kMaxDevices][kVariants][kSortClasses];
 
 int variant_index(int head_dim, int mode) { return (head_dim == 64 ? 0 : 1) + 2 * mode; }
 
@@ -1224,23 +1226,35 @@ int launch_fwd(Params prm, int mode, int max_seqlen_q, int head_dim, hipStream_t
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
   if (rc != PFA_OK) return rc;
+  // Schedule capacity: the streaming kernel's LDS grows (two ints per entry) so that tables
+  // of up to kSortCapMax segments are sorted longest-first; the resident kernel's LDS is
+  // full and keeps kSortMax.  Beyond the capacity the kernels walk the unsorted slots.
+  int cap = kSortMax, cls = 0;
+  if (mode != kModeResident && prm.num_seqs > kSortMax && prm.num_seqs <= kSortCapMax)
+    while (cap < prm.num_seqs) {
+      cap <<= 1;
+      ++cls;
+    }
+  const size_t lds = var.lds + sizeof(int) * 2 * (size_t)(cap - kSortMax);
+  const size_t lds_max = mode == kModeResident ? var.lds : var.lds + sizeof(int) * 2 * (size_t)(kSortCapMax - kSortMax);
   const int vi = variant_index(head_dim, mode);
-  int occ = g_occ[dev][vi].load(std::memory_order_relaxed);
+  int occ = g_occ[dev][vi][cls].load(std::memory_order_relaxed);
   if (occ <= 0) {
-    if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)var.lds) != hipSuccess)
+    if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max) != hipSuccess)
       return PFA_ERR_DEVICE;
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, var.threads, var.lds) != hipSuccess || o <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, var.fn, var.threads, lds) != hipSuccess || o <= 0)
       return PFA_ERR_DEVICE;
     occ = o;
-    g_occ[dev][vi].store(occ, std::memory_order_relaxed);
+    g_occ[dev][vi][cls].store(occ, std::memory_order_relaxed);
   }
   int64_t grid = (int64_t)cus * occ;
   if (grid > slots) grid = slots;
   if (grid >= 8) grid -= grid % 8;   // keep whole rounds on every XCD
   prm.qt_max = (int)qt_max;
+  prm.sort_cap = cap;
   void* args[] = {&prm};
-  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, var.lds, stream);
+  const hipError_t err = hipLaunchKernel(var.fn, dim3((unsigned)grid), dim3(var.threads), args, lds, stream);
   return err == hipSuccess ? PFA_OK : PFA_ERR_LAUNCH;
 }
 

@@ -49,12 +49,24 @@ def test_tile_boundaries_full(lengths):
         _full_check(wl, f"edges {lengths} d={d}")
 
 
-def test_many_segments_unsorted_mode():
-    """More segments than the on-device sorter handles: the slot scheduler path."""
+def test_many_segments_bitonic_schedule():
+    """Over 512 segments the schedule is sorted by a bitonic network in LDS (capacity 2048
+    here)."""
     rng = np.random.default_rng(5)
     lengths = [int(x) for x in rng.integers(0, 40, size=1100)]
     wl = W.make(lengths, 2, 64, seed=5, name="1100 segments")
     _full_check(wl, "1100 segments d64")
+
+
+@pytest.mark.parametrize("n,d", [(4096, 128), (4097, 64), (5000, 128)])
+def test_segments_at_and_beyond_the_sort_capacity(n, d):
+    """4,096 segments fill the largest schedule capacity; above it the kernel walks the
+    unsorted (segment, head, tile) slots."""
+    rng = np.random.default_rng(8 + n)
+    lengths = [int(x) for x in rng.integers(0, 48, size=n)]
+    lengths[int(rng.integers(0, n))] = 700          # one multi-tile segment among them
+    wl = W.make(lengths, 1, d, seed=8 + n, name=f"{n} segments")
+    _full_check(wl, f"{n} segments d{d}")
 
 
 def test_many_segments_sorted_mode():

@@ -131,7 +131,7 @@ def test_without_lse_and_binding_checks():
         pfa_varlen_fwd_qkv(qkv[:, :2], cu, wl.max_seqlen)                   # not [T, 3, H, d]
 
 
-def test_many_segments_unsorted_schedule_with_rope():
+def test_many_segments_bitonic_schedule_with_rope():
     rng = np.random.default_rng(35)
     lengths = [int(x) for x in rng.integers(0, 200, size=600)]
     wl = W.make(lengths, 2, 128, seed=35, name="600 segments")

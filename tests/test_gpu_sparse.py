@@ -124,13 +124,13 @@ def test_determinism_and_binding_checks():
         pfa_varlen_fwd_blocksparse(q, q, q, cu, wl.max_seqlen, p, i)
 
 
-def test_many_segments_unsorted_schedule():
-    # over 512 segments the kernel enumerates (segment, head, tile) slots instead of sorting
+def test_many_segments_bitonic_schedule():
+    # over 512 segments the schedule is sorted by a bitonic network (capacity 1024 here)
     rng = np.random.default_rng(315)
     lengths = [int(x) for x in rng.integers(0, 300, size=700)]
     wl = W.make(lengths, 2, 128, seed=315, name="700 segments")
     lay = W.random_layout(rng, wl.lengths, 1, density=0.7)
-    _check(wl, lay, "700 segments, unsorted schedule")
+    _check(wl, lay, "700 segments, bitonic schedule")
 
 
 def test_poison_in_other_segments_does_not_leak():
