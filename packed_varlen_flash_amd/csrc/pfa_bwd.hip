@@ -155,7 +155,7 @@ __device__ __forceinline__ void bwd_prep_row(const BwdParams& p, int T, int64_t 
 
 template <int D>
 __global__ void __launch_bounds__(256) pfa_bwd_prep_kernel(BwdParams p) {
-  const int T = p.cu[p.num_seqs];   // T is known only on the device
+  const int T = ld_table(p.cu, p.num_seqs);   // T is known only on the device
   if (T > p.ws_rows) return;
   for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < (int64_t)T * p.heads;
        row += (int64_t)gridDim.x * 256)
@@ -172,11 +172,11 @@ __device__ __forceinline__ bool bwd_item(const BwdParams& p, int u, bool sorted,
     int lo = 0, hi = p.num_seqs - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (s_prefix[mid] <= u) lo = mid; else hi = mid - 1;
+      if (__builtin_amdgcn_readfirstlane(s_prefix[mid]) <= u) lo = mid; else hi = mid - 1;
     }
-    s = s_order[lo];
-    const int ntiles = (p.cu[s + 1] - p.cu[s] + BT - 1) / BT;
-    const int local = u - s_prefix[lo];
+    s = __builtin_amdgcn_readfirstlane(s_order[lo]);
+    const int ntiles = (ld_table(p.cu, s + 1) - ld_table(p.cu, s) + BT - 1) / BT;
+    const int local = u - __builtin_amdgcn_readfirstlane(s_prefix[lo]);
     h = local / ntiles;
     tile = local - h * ntiles;
   } else {
@@ -186,8 +186,8 @@ __device__ __forceinline__ bool bwd_item(const BwdParams& p, int u, bool sorted,
     h = rem / p.tiles_max;
     tile = rem - h * p.tiles_max;
   }
-  a = p.cu[s];
-  L = p.cu[s + 1] - a;
+  a = ld_table(p.cu, s);
+  L = ld_table(p.cu, s + 1) - a;
   if (a < 0 || a >= T) return false;
   if (L > T - a) L = T - a;
   return L > 0 && tile * BT < L;
@@ -241,7 +241,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
   int* s_prefix = s_order + kSortMax;
   int* s_len = reinterpret_cast<int*>(qring);
 
-  const int T = p.cu[p.num_seqs];
+  const int T = ld_table(p.cu, p.num_seqs);
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
@@ -407,7 +407,7 @@ pfa_bwd_dq_kernel(BwdParams p) {
   int* s_prefix = s_order + kSortMax;
   int* s_len = reinterpret_cast<int*>(kring);
 
-  const int T = p.cu[p.num_seqs];
+  const int T = ld_table(p.cu, p.num_seqs);
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
   const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,

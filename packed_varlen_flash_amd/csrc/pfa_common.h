@@ -37,6 +37,14 @@ constexpr int kWaitVmem = 0x0F70;   // s_waitcnt vmcnt(0), other counters uncons
 // s_waitcnt vmcnt(n), other counters unconstrained (vmcnt bits 3:0 and 15:14)
 constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
+// Entry i of a read-only int32 table (the segment tables), i wave-uniform: read through
+// the scalar cache (constant address space), so its wait is on lgkmcnt and never on the
+// vector-memory counter, which also counts the output stores still in flight.
+typedef const __attribute__((address_space(4))) int32_t cint32_t;
+__device__ __forceinline__ int32_t ld_table(const int32_t* t, int i) {
+  return ((cint32_t*)t)[i];   // an address-space cast (reinterpret_cast cannot express it)
+}
+
 // a pointer the caller knows to be wave-uniform, in scalar registers (a buffer resource
 // built from it then needs no per-lane loop)
 __device__ __forceinline__ void* uniform_ptr(const void* ptr) {

@@ -703,8 +703,8 @@ pfa_fwd_kernel(Params p) {
   int* s_blk = s_order + 2 * p.sort_cap + 8;   // block-sparse variant only (its LDS is larger)
   int* s_len = reinterpret_cast<int*>(ks);     // scratch, dead before the first K tile lands
 
-  const int Tq = p.cu_q[p.num_seqs];
-  const int Tk = cu_k[p.num_seqs];
+  const int Tq = ld_table(p.cu_q, p.num_seqs);
+  const int Tk = ld_table(cu_k, p.num_seqs);
   const bool sorted = p.num_seqs <= p.sort_cap;
   int total;
   if (sorted) {
@@ -728,11 +728,11 @@ pfa_fwd_kernel(Params p) {
       int lo = 0, hi = p.num_seqs - 1;   // last rank r with s_prefix[r] <= u
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (s_prefix[mid] <= u) lo = mid; else hi = mid - 1;
+        if (__builtin_amdgcn_readfirstlane(s_prefix[mid]) <= u) lo = mid; else hi = mid - 1;
       }
-      s = s_order[lo];
-      const int ntiles = (p.cu_q[s + 1] - p.cu_q[s] + C::BM - 1) / C::BM;
-      const int local = u - s_prefix[lo];
+      s = __builtin_amdgcn_readfirstlane(s_order[lo]);
+      const int ntiles = (ld_table(p.cu_q, s + 1) - ld_table(p.cu_q, s) + C::BM - 1) / C::BM;
+      const int local = u - __builtin_amdgcn_readfirstlane(s_prefix[lo]);
       h = local / ntiles;
       qt = local - h * ntiles;
     } else {
@@ -742,16 +742,16 @@ pfa_fwd_kernel(Params p) {
       h = rem / p.qt_max;
       qt = rem - h * p.qt_max;
     }
-    const int qa = p.cu_q[s];
-    int Lq = p.cu_q[s + 1] - qa;
+    const int qa = ld_table(p.cu_q, s);
+    int Lq = ld_table(p.cu_q, s + 1) - qa;
     // never touch rows outside [0, Tq) / [0, Tk), whatever the tables say
     if (qa < 0 || qa >= Tq) continue;
     if (Lq > Tq - qa) Lq = Tq - qa;
     if (Lq <= 0 || qt * C::BM >= Lq) continue;
     int ka = qa, Lk = Lq;
     if (MODE == kModeCross) {
-      ka = cu_k[s];
-      Lk = cu_k[s + 1] - ka;
+      ka = ld_table(cu_k, s);
+      Lk = ld_table(cu_k, s + 1) - ka;
       if (ka < 0 || ka > Tk) ka = Tk;
       if (Lk > Tk - ka) Lk = Tk - ka;
       if (Lk < 0) Lk = 0;
@@ -850,8 +850,8 @@ pfa_fwd_resident_kernel(Params p) {
   const int kbytes = (int)(rs * 2);
   const float c = p.c;
 
-  const int Tq = p.cu_q[p.num_seqs];
-  const int Tk = p.cu_k[p.num_seqs];
+  const int Tq = ld_table(p.cu_q, p.num_seqs);
+  const int Tk = ld_table(p.cu_k, p.num_seqs);
   const bool sorted = p.num_seqs <= kSortMax;
   // Item decoding reads the segment tables from LDS (sorted mode), so that no vector-memory
   // load sits between the next tile's Q loads and the wait for them.
@@ -918,8 +918,8 @@ pfa_fwd_resident_kernel(Params p) {
       const int rem = (int)u - it.s * per_seg;
       it.h = rem / p.qt_max;
       it.qt = rem - it.h * p.qt_max;
-      it.qa = rfl(p.cu_q[it.s]);
-      qe = rfl(p.cu_q[it.s + 1]);
+      it.qa = ld_table(p.cu_q, it.s);
+      qe = ld_table(p.cu_q, it.s + 1);
     }
     return rows_of(it, qe);
   };
@@ -976,8 +976,8 @@ pfa_fwd_resident_kernel(Params p) {
       ka = rfl(s_cuk[s_]);
       len = rfl(s_cuk[s_ + 1]) - ka;
     } else {
-      ka = rfl(p.cu_k[s_]);
-      len = rfl(p.cu_k[s_ + 1]) - ka;
+      ka = ld_table(p.cu_k, s_);
+      len = ld_table(p.cu_k, s_ + 1) - ka;
       // keeps the two branches' loads apart: merged, they become one generic-address load
       // whose wait would take in the next tile's Q loads
       asm volatile("" ::: "memory");
