@@ -212,6 +212,7 @@ __device__ __forceinline__ void bwd_issue_tile(const __bf16* base, int r0, int L
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, src[i], 0, 0, 0);
 }
 
+
 // Order of a contraction whose 16-deep steps each read two operand fragments from LDS
 // (in consumption order) and issue two MFMAs: the reads run `ahead` steps before the MFMAs
 // that consume them.  With one wave per SIMD nothing else hides the read latency.
@@ -226,7 +227,7 @@ __device__ __forceinline__ void pair_read_ahead() {
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * AHEAD, 0);
 }
-constexpr int kDkdvReadAhead = 3;
+constexpr int kDkdvReadAhead = 2;
 
 // ---- dK / dV
 template <int D>
@@ -326,26 +327,29 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
       const char* dst = dring + cur * C::TILE_BYTES;
       const float* nls = reinterpret_cast<const float*>(fring + (cur * 2) * C::ROWF_BYTES);
       const float* dls = reinterpret_cast<const float*>(fring + (cur * 2 + 1) * C::ROWF_BYTES);
+      // Both sub-blocks' S and dP products first, then per sub-block the weights and the dV,
+      // dK products: the second pair of products runs in the matrix pipe while the first
+      // sub-block's weights are formed, and the first sub-block's dV/dK products while the
+      // second's are.  One wave per SIMD has no partner to fill those gaps.
+      f32x16 sc[2], dp[2];
 #pragma unroll
-      for (int j = 0; j < kBwdStage / 32; ++j) {
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 qa[C::KSTEP], da[C::KSTEP];
+        k_operands2<D>(qst + j * 32 * D * 2, dst + j * 32 * D * 2, koff, qa, da);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[j][i] = dp[j][i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < C::KSTEP; ++t) {
+          sc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], kr[t], sc[j], 0, 0, 0);
+          dp[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], vr[t], dp[j], 0, 0, 0);
+        }
+        pair_read_ahead<D, kDkdvReadAhead>();   // each pair's operand reads run two steps ahead
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
         const char* qj = qst + j * 32 * D * 2;
         const char* dj = dst + j * 32 * D * 2;
-        f32x16 sc, dp;
-        __builtin_amdgcn_sched_barrier(0);   // the S / dP products form a region of their own
-        {
-          bf16x8 qa[C::KSTEP], da[C::KSTEP];
-          k_operands2<D>(qj, dj, koff, qa, da);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = dp[i] = 0.f;
-#pragma unroll
-          for (int t = 0; t < C::KSTEP; ++t) {
-            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[t], kr[t], sc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[t], vr[t], dp, 0, 0, 0);
-          }
-          pair_read_ahead<D, kDkdvReadAhead>();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // element i holds query row j*32 + 8(i/4) + 4g + i%4 of this key column
         bf16x8 pp[2], dsp[2];
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
@@ -357,8 +361,8 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 4 * a4 + e;
-            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[i], p.c, nlv[e]));
-            const float dsv = pv * (dp[i] - dlv[e]);
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[j][i], p.c, nlv[e]));
+            const float dsv = pv * (dp[j][i] - dlv[e]);
             pp[i >> 3][i & 7] = (__bf16)pv;
             dsp[i >> 3][i & 7] = (__bf16)dsv;
           }
