@@ -24,7 +24,6 @@ row sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -44,19 +43,20 @@ LIBRARY = os.path.join(ROOT, "packed_varlen_flash_amd", "libpfa.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_pfa_fwd_C3.json")
 
 
-def library_sha() -> str:
-    with open(LIBRARY, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def measured_traffic(config: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken
-    on the library binary as it is now (the build is deterministic); otherwise None."""
-    if config != "C3" or not os.path.exists(TRAFFIC_FILE) or not os.path.exists(LIBRARY):
+    on the forward kernel as it is now: the record's hash of the forward sources must
+    equal both the sources' present hash and the one the built library recorded (the
+    build is deterministic); otherwise None."""
+    if config != "C3" or not os.path.exists(TRAFFIC_FILE) or not os.path.exists(LIBRARY + ".fwdsha"):
         return None
+    from packed_varlen_flash_amd.build import forward_sources_sha
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("library_sha256") != library_sha():
+    with open(LIBRARY + ".fwdsha") as f:
+        built = f.read().strip()
+    now = forward_sources_sha()
+    if t.get("forward_sources_sha256") != now or built != now:
         return None
     return t.get("hbm_bytes_per_launch")
 

@@ -26,15 +26,32 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (need ROCm with gfx950 support)")
 
 
+# compiler options of every kernel (gfx950 code generation)
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden", "-fno-honor-nans",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# what the forward kernel's code depends on: a built library records its hash beside
+# itself, so that a measurement taken on one build can be matched to a later build of the
+# same forward kernel (the build is deterministic)
+FWD_SOURCES = [os.path.join(CSRC, "pfa_fwd.hip"), os.path.join(CSRC, "pfa_common.h"),
+               os.path.join(INCLUDE, "pfa.h")]
+
+
+def forward_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256(" ".join([ARCH, *FLAGS]).encode())
+    for path in FWD_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def build(verbose: bool = False, sanitize_host: bool = False, path: str | None = None) -> str:
     """sanitize_host: compile the host code (argument checks, validators, launch setup)
     with AddressSanitizer and UndefinedBehaviorSanitizer; the GPU code is built as always.
     Loading such a library needs clang's ASan runtime preloaded.  path: output file."""
     out = path or LIB
     tmp = out + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-fvisibility=hidden", "-fno-honor-nans", "-I", INCLUDE, "-I", CSRC,
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", *FLAGS, "-I", INCLUDE, "-I", CSRC]
     if sanitize_host:
         cmd += ["-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-sanitize-recover=all",
                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
@@ -45,6 +62,8 @@ def build(verbose: bool = False, sanitize_host: bool = False, path: str | None =
     if verbose:
         print(res.stderr)
     os.replace(tmp, out)
+    with open(out + ".fwdsha", "w") as f:      # the forward sources this build came from
+        f.write(forward_sources_sha() + "\n")
     return out
 
 
