@@ -241,3 +241,28 @@ def test_resident_kv_switching_matches_the_streaming_kernel_bitwise(d):
     # and the resident kernel against the oracle on sampled rows of every segment
     rows = W.sample_rows(x.cu_q, stride=97, edge=8, full_upto=0)
     _check(x, f"resident-switch d={d} sampled {len(rows)} rows", rows=rows)
+
+
+@pytest.mark.parametrize("n,d", [(600, 128), (700, 64), (4200, 128)])
+def test_many_segments_resident_and_streaming_schedules(n, d):
+    """Over 512 segments the resident kernel walks the unsorted slots while the streaming
+    kernel sorts them (bitonic, up to 4,096) or also walks them (4,200): every tile is
+    computed once whatever the order, so the two kernels agree bitwise, and a sample of rows
+    against the oracle."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd_qk
+    kmax = 256 if d == 128 else 128
+    rng = np.random.default_rng(800 + n)
+    lq = [int(x) for x in rng.integers(0, 300, size=n)]
+    lk = [int(x) for x in rng.integers(0, kmax + 1, size=n)]
+    lq[int(rng.integers(0, n))] = 1500                # one multi-tile query segment
+    x = W.make_cross(lq, lk, 2, d, seed=800 + n, name=f"{n} cross segments")
+    q, k, v, cq, ck = _upload(x)
+    say(f"[gpu] {n} cross segments d={d}: resident (unsorted) vs streaming")
+    o1, l1 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax, x.scale)        # resident
+    o2, l2 = pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, kmax + 1, x.scale)    # streaming
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    rows = W.sample_rows(x.cu_q, stride=53, edge=4, full_upto=0)
+    _check(x, f"{n} cross segments d={d} sampled {len(rows)} rows", rows=rows)
