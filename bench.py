@@ -131,6 +131,27 @@ def cpu_baseline(wl, out_bits, lse, budget_s: float):
 PEAK_HBM_GBS = 8000.0                # MI355X HBM3E (published)
 
 
+WARMUP_MIN, WARMUP_SECONDS = 50, 0.15
+
+
+def resolve_warmup(args, step, stream):
+    """The number of untimed warm-up steps: --warmup if given, else enough launches to keep
+    the GPU busy for WARMUP_SECONDS (at least WARMUP_MIN), so that the timed steps run at
+    the settled clock rather than in the ramp after idle.  The count is what the JSON line
+    reports as "warmup"."""
+    import torch
+    if args.warmup is None:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        step()
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        one_ms = max(e0.elapsed_time(e1), 1e-3)
+        args.warmup = int(min(20000, max(WARMUP_MIN, math.ceil(WARMUP_SECONDS * 1e3 / one_ms))))
+    return args.warmup
+
+
 def timed(step, stream, steps, warmup):
     """W untimed steps, then K timed steps bracketed by synchronisation; returns (wall ms per
     step, kernel ms per step from HIP events recorded on the launch stream)."""
@@ -183,6 +204,7 @@ def bench_cross(args):
     def step():
         pfa_varlen_fwd_qk(q, k, v, cq, ck, x.max_q, x.max_k, x.scale, out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step, stream)
     ms, kms = timed(step, stream, args.steps, args.warmup)
 
     # the streaming kernel on the same pack, for comparison: a key bound above the
@@ -276,6 +298,7 @@ def bench_merge(args):
     def step():
         pfa_attn_merge(oa, la, ob, lb, out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step, stream)
     ms, kms = timed(step, stream, args.steps, args.warmup)
     alg = T * H * (3 * 2 * d + 3 * 4)
     cpu = parity = None
@@ -333,6 +356,7 @@ def bench_bwd(args):
         pfa_varlen_bwd(q, k, v, out, do, lse, cu, wl.max_seqlen, wl.scale, dq=dq, dk=dk, dv=dv,
                        workspace=ws, stream=stream)
 
+    resolve_warmup(args, step, stream)
     ms, kms = timed(step, stream, args.steps, args.warmup)
     counted = 2.5 * wl.flops
     executed = 3.5 * wl.flops
@@ -411,6 +435,7 @@ def bench_qkv(args):
         pfa_varlen_fwd(rope_torch(q3), rope_torch(k3), v3.contiguous(), cu, wl.max_seqlen, wl.scale,
                        out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step_plain, stream)
     ms_plain, kms_plain = timed(step_plain, stream, args.steps, args.warmup)
     ms_unf, _ = timed(step_unfused, stream, args.steps, args.warmup)
     ms, kms = timed(step, stream, args.steps, args.warmup)
@@ -495,6 +520,7 @@ def bench_fps(args):
     def step_dense():
         pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step_dense, stream)
     ms_dense, _ = timed(step_dense, stream, args.steps, args.warmup)
     ms_sp, _ = timed(step_sparse_bf16, stream, args.steps, args.warmup)
     ms, kms = timed(step, stream, args.steps, args.warmup)
@@ -579,6 +605,7 @@ def bench_sparse(args):
     def step_dense():
         pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step_dense, stream)
     ms_dense, _ = timed(step_dense, stream, args.steps, args.warmup)
     ms, kms = timed(step, stream, args.steps, args.warmup)
     cpu = parity = None
@@ -670,6 +697,7 @@ def bench_fp8pv(args):
     def step_bf16():
         pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
 
+    resolve_warmup(args, step_bf16, stream)
     ms_bf16, _ = timed(step_bf16, stream, args.steps, args.warmup)
     ms_q, _ = timed(quant, stream, args.steps, args.warmup)
     ms, kms = timed(step, stream, args.steps, args.warmup)
@@ -742,7 +770,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps (default: enough for 0.15 s of GPU work, at least 50)")
     ap.add_argument("--config", default="C3", choices=sorted(W.CONFIGS) + sorted(W.CROSS_CONFIGS))
     ap.add_argument("--op", default="fwd", choices=["fwd", "merge", "bwd", "qkv", "sparse", "fp8pv", "fps"])
     ap.add_argument("--band", type=int, default=1024, help="band radius (tokens) for --op sparse")
@@ -802,7 +831,7 @@ def main():
     def step():
         pfa_varlen_fwd(q, k, v, cu, wl.max_seqlen, wl.scale, out=out, lse=lse, stream=stream)
 
-    for _ in range(args.warmup):
+    for _ in range(resolve_warmup(args, step, stream)):
         step()
     torch.cuda.synchronize()
 
