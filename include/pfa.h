@@ -325,9 +325,9 @@ PFA_API int pfa_attn_merge(const void* o_a, const float* lse_a, const void* o_b,
  * workspace   device fp32 [2, heads, T], written: -lse*log2(e) and delta.  The caller
  *             owns it; its contents after the call are not part of the interface.
  * Ownership and errors as for pfa_varlen_fwd; PFA_ERR_ALIAS if an output (dq, dk, dv,
- * workspace) is an input or another output.  Three kernels are enqueued on stream (a
- * row-statistics pass, the dK/dV pass, the dQ pass); no atomics, so results are
- * deterministic.
+ * workspace) is an input or another output.  Two kernels are enqueued on stream (the dQ
+ * pass, which also writes the row statistics to workspace, then the dK/dV pass, which
+ * reads them); no atomics, so results are deterministic.
  */
 PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
                            const void* dout, const float* lse, const int32_t* cu_seqlens,
@@ -341,7 +341,7 @@ PFA_API int pfa_varlen_bwd(const void* q, const void* k, const void* v, const vo
 /*
  * pfa_varlen_bwd_noalloc -- pfa_varlen_bwd for callers that cannot allocate device memory
  * (code under graph capture, tight serving or training loops, harnesses that forbid
- * allocation): the same gradients from the same three kernels, with the 2 * heads * T fp32
+ * allocation): the same gradients from the same two kernels, with the 2 * heads * T fp32
  * row statistics kept in a library-held device array instead of a caller workspace.
  *
  * The array holds PFA_BWD_SCRATCH_FLOATS values (32 MiB), one copy per device the

@@ -12,15 +12,15 @@ namespace {
 // the forward definition gives (per segment and head)
 //     dV = P^T dO,  dP = dO V^T,  delta_i = sum_j P_ij dP_ij = dO_i . O_i,
 //     dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q.
-// Three launches, no atomics and no scratch of the library's own:
-//   * prep: ws[0] = -LSE * log2(e) and ws[1] = delta = rowsum(dO * O), fp32 [H, T] each,
-//     in the caller's workspace;
-//   * dK/dV: one work item = 128 keys of one (segment, head), stationary in VGPRs as the
+// Two launches, no atomics and no scratch of the library's own:
+//   * dQ (first): one work item = 128 queries; the forward's shape: S^T = K Q^T, dP^T = V dO^T
+//     (lanes hold queries), dQ^T += K^T dS^T with K^T from transposed LDS reads.  It also
+//     writes each query row's statistics, ws[0] = -LSE * log2(e) and ws[1] = delta =
+//     rowsum(dO * O), fp32 [H, T] each, to the caller's workspace;
+//   * dK/dV (second, reading ws): one work item = 128 keys of one (segment, head), stationary in VGPRs as the
 //     B operands of S = Q K^T and dP = dO V^T (lanes hold keys); the segment's Q and dO
 //     stream through LDS in 64-row stages; dV^T += dO^T P and dK^T += Q^T dS take their
-//     A operands from transposed LDS reads of the same stages;
-//   * dQ: one work item = 128 queries; the forward's shape: S^T = K Q^T, dP^T = V dO^T
-//     (lanes hold queries), dQ^T += K^T dS^T with K^T from transposed LDS reads.
+//     A operands from transposed LDS reads of the same stages.
 // Every stage tile is read both as rows and transposed, so it is stored in the KV swizzle,
 // free of bank conflicts for both patterns; the transposed reads take explicit per-lane
 // offsets for each 16-row step and 8-row half, since the swizzle does not keep a constant
@@ -131,35 +131,6 @@ __device__ __forceinline__ void store_rows(const char* ost, int lane, __bf16* ds
     const u32x4 x = *reinterpret_cast<const u32x4*>(ost + phys_off<D, Swz::K>(r, ch));
     if (r < valid) *reinterpret_cast<u32x4*>(dst + (int64_t)r * rs + ch * 8) = x;
   }
-}
-
-// prep: ws[0][h][t] = -LSE[h][t] * log2(e); ws[1][h][t] = sum_d dO[t,h,d] O[t,h,d].
-// One thread per (token, head) row, grid-stride over T * heads rows.
-template <int D>
-__device__ __forceinline__ void bwd_prep_row(const BwdParams& p, int T, int64_t row) {
-  const int64_t t = row / p.heads;
-  const int h = (int)(row - t * p.heads);
-  const bf16x8* o = reinterpret_cast<const bf16x8*>(p.out + row * D);
-  const bf16x8* d = reinterpret_cast<const bf16x8*>(p.dout + row * D);
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 a = o[c], b = d[c];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf((float)a[e], (float)b[e], acc);
-  }
-  const int64_t idx = (int64_t)h * T + t;
-  p.ws[idx] = -p.lse[idx] * kLog2e;
-  p.ws[(int64_t)p.heads * T + idx] = acc;
-}
-
-template <int D>
-__global__ void __launch_bounds__(256) pfa_bwd_prep_kernel(BwdParams p) {
-  const int T = ld_table(p.cu, p.num_seqs);   // T is known only on the device
-  if (T > p.ws_rows) return;
-  for (int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x; row < (int64_t)T * p.heads;
-       row += (int64_t)gridDim.x * 256)
-    bwd_prep_row<D>(p, T, row);
 }
 
 // Decode work item u of a sorted or slot-enumerated schedule into (segment start, length,
@@ -460,8 +431,25 @@ pfa_bwd_dq_kernel(BwdParams p) {
         dr[t] = __builtin_bit_cast(bf16x8, y);
       }
     }
-    const float nl = row < L ? p.ws[(int64_t)h * T + a + row] : 0.f;
-    const float dl = row < L ? p.ws[(int64_t)p.heads * T + (int64_t)h * T + a + row] : 0.f;
+    // The row statistics of this lane's query, for this pass and the dK/dV pass after it:
+    // nl = -LSE * log2(e) and delta = dO . O.  The lane holds half of the row (values
+    // 16t + 8g .. +7, the layout of dr); lanes n32 and n32 + 32 add their halves.
+    float nl = 0.f, part = 0.f;
+    if (row < L) {
+      const __bf16* op = p.out + (int64_t)(a + row) * rs + head_off;
+#pragma unroll
+      for (int t = 0; t < C::KSTEP; ++t) {
+        const bf16x8 o = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * t + 8 * g));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf((float)o[e], (float)dr[t][e], part);
+      }
+      nl = -p.lse[(int64_t)h * T + a + row] * kLog2e;
+    }
+    const float dl = part + __shfl_xor(part, 32);
+    if (g == 0 && row < L) {
+      p.ws[(int64_t)h * T + a + row] = nl;
+      p.ws[(int64_t)p.heads * T + (int64_t)h * T + a + row] = dl;
+    }
     f32x16 dqt[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
@@ -591,7 +579,7 @@ int check_bwd_args(const void* q, const void* k, const void* v, const void* out,
   return PFA_OK;
 }
 
-// The three backward launches, with the row statistics in ws (room for ws_rows tokens).
+// The two backward launches, with the row statistics in ws (room for ws_rows tokens).
 int launch_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
                const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
                int head_dim, float scale, void* dq, void* dk, void* dv, float* ws, int ws_rows,
@@ -601,8 +589,6 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
   if (rc != PFA_OK) return rc;
-  const void* prep = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_prep_kernel<64>)
-                                    : reinterpret_cast<const void*>(&pfa_bwd_prep_kernel<128>);
   const void* dkdv = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_dkdv_kernel<64>)
                                     : reinterpret_cast<const void*>(&pfa_bwd_dkdv_kernel<128>);
   const void* dqk = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_dq_kernel<64>)
@@ -650,11 +636,10 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   bp.c = scale * kLog2e;
   bp.scale = scale;
   void* args[] = {&bp};
-  if (hipLaunchKernel(prep, dim3((unsigned)cus * 8), dim3(256), args, 0, stream) != hipSuccess)
+  // dQ first: it writes the row statistics the dK/dV pass reads
+  if (hipLaunchKernel(dqk, dim3(grid_for(occ_q)), dim3(threads), args, lds_dq, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   if (hipLaunchKernel(dkdv, dim3(grid_for(occ_kv)), dim3(threads), args, lds_dkdv, stream) != hipSuccess)
-    return PFA_ERR_LAUNCH;
-  if (hipLaunchKernel(dqk, dim3(grid_for(occ_q)), dim3(threads), args, lds_dq, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   return PFA_OK;
 }
