@@ -201,8 +201,14 @@ __device__ __forceinline__ void pair_read_ahead() {
 constexpr int kDkdvReadAhead = 2;
 
 // ---- dK / dV
+// Waves per SIMD the dK/dV kernel is compiled for: at d = 128 it needs ~450 registers
+// (one wave); at d = 64 the same code fits 256 without spills, so two workgroups share a CU.
 template <int D>
-__global__ void __launch_bounds__(kWave * kBwdNW) __attribute__((amdgpu_waves_per_eu(1, 1)))
+constexpr int kDkdvWavesPerEu = D == 64 ? 2 : 1;
+
+template <int D>
+__global__ void __launch_bounds__(kWave * kBwdNW)
+__attribute__((amdgpu_waves_per_eu(kDkdvWavesPerEu<D>, kDkdvWavesPerEu<D>)))
 pfa_bwd_dkdv_kernel(BwdParams p) {
   using C = BwdTile<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
