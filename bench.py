@@ -334,8 +334,8 @@ def bench_merge(args):
 
 
 def bench_bwd(args):
-    """Backward of the forward on the same pack: three kernels per step (row statistics,
-    dK/dV, dQ).  Counted work 10*sum(L^2)*H*d (five L x L x d matmuls, the usual count);
+    """Backward of the forward on the same pack: two kernels per step (dQ with the row
+    statistics, then dK/dV).  Counted work 10*sum(L^2)*H*d (five L x L x d matmuls, the usual count);
     this design executes seven (S and dP are recomputed in each of the two passes)."""
     import torch
     from packed_varlen_flash_amd import pfa_varlen_bwd, pfa_varlen_fwd
