@@ -13,7 +13,7 @@ namespace {
 //     dV = P^T dO,  dP = dO V^T,  delta_i = sum_j P_ij dP_ij = dO_i . O_i,
 //     dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q.
 // Two launches, no atomics and no scratch of the library's own:
-//   * dQ (first): one work item = 128 queries; the forward's shape: S^T = K Q^T, dP^T = V dO^T
+//   * dQ (first): one work item = 256 queries; the forward's shape: S^T = K Q^T, dP^T = V dO^T
 //     (lanes hold queries), dQ^T += K^T dS^T with K^T from transposed LDS reads.  It also
 //     writes each query row's statistics, ws[0] = -LSE * log2(e) and ws[1] = delta =
 //     rowsum(dO * O), fp32 [H, T] each, to the caller's workspace;
@@ -26,12 +26,16 @@ namespace {
 // offsets for each 16-row step and 8-row half, since the swizzle does not keep a constant
 // pattern 8 rows apart.
 // ---------------------------------------------------------------------------------
-// waves per workgroup (one per SIMD).  dK/dV holds two accumulators and the stationary K
-// and V fragments (428 registers at d = 128), so one workgroup fills a CU; dQ loads its
-// two operand sets one after the other and fits 256 registers, so two workgroups share a
-// CU (its few spills are per-item offsets, reloaded outside the stage loop).
+// Waves per workgroup.  dK/dV: four, one per SIMD; it holds two accumulators and the
+// stationary K and V fragments (450 registers at d = 128), so one workgroup fills a CU
+// (at d = 64 it fits 256 registers and two workgroups share a CU).  dQ: eight, two per
+// SIMD; it loads its two operand sets one after the other and fits 256 registers (its few
+// spills are per-item offsets, reloaded outside the stage loop), and one K/V stage load
+// feeds 256 queries.
 constexpr int kBwdNW = 4;
-constexpr int kBwdRows = kBwdNW * 32;      // keys (dK/dV) or queries (dQ) per work item
+constexpr int kBwdRows = kBwdNW * 32;      // keys per dK/dV work item
+constexpr int kDqNW = 8;
+constexpr int kDqRows = kDqNW * 32;        // queries per dQ work item
 constexpr int kBwdStage = 64;              // rows per streamed stage
 
 struct BwdParams {
@@ -49,14 +53,15 @@ struct BwdParams {
   __bf16* dv;
   int num_seqs;
   int heads;
-  int tiles_max;          // ceil(max_seqlen / kBwdRows): slots per (segment, head), unsorted mode
+  int tiles_max;          // ceil(max_seqlen / kBwdRows): dK/dV slots per (segment, head), unsorted mode
+  int tiles_max_q;        // ceil(max_seqlen / kDqRows): the same for dQ
   float c;                // scale * log2(e)
   float scale;
 };
 
-template <int D>
+template <int D, int NW = kBwdNW>
 struct BwdTile {
-  static constexpr int THREADS = kWave * kBwdNW;
+  static constexpr int THREADS = kWave * NW;
   static constexpr int CPR = D / 8;                          // 16-byte chunks per row
   static constexpr int TILE_BYTES = kBwdStage * D * 2;       // one 64-row bf16 tile
   static constexpr int CPT = kBwdStage * CPR / THREADS;      // chunks per thread per tile
@@ -69,7 +74,7 @@ struct BwdTile {
   // dQ: [K ring][V ring] + schedule
   static constexpr size_t LDS_DQ = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * (2 * kSortMax + 8);
   static_assert(CPT * THREADS == kBwdStage * CPR, "stage must split evenly");
-  static_assert(kBwdNW * 32 * D * 2 * 2 <= kStages * 2 * TILE_BYTES, "two output blocks fit the ring");
+  static_assert(NW * 32 * D * 2 <= kStages * 2 * TILE_BYTES, "one output block per wave fits the ring");
 };
 
 // Transposed A-operand reads of one 32-row sub-block (rows of the tile = the MFMA's k):
@@ -136,7 +141,7 @@ __device__ __forceinline__ void store_rows(const char* ost, int lane, __bf16* ds
 // Decode work item u of a sorted or slot-enumerated schedule into (segment start, length,
 // head, tile); false if the item is empty.
 template <int BT>
-__device__ __forceinline__ bool bwd_item(const BwdParams& p, int u, bool sorted, const int* s_order,
+__device__ __forceinline__ bool bwd_item(const BwdParams& p, int tiles_max, int u, bool sorted, const int* s_order,
                                          const int* s_prefix, int T, int& a, int& L, int& h, int& tile) {
   int s;
   if (sorted) {
@@ -151,11 +156,11 @@ __device__ __forceinline__ bool bwd_item(const BwdParams& p, int u, bool sorted,
     h = local / ntiles;
     tile = local - h * ntiles;
   } else {
-    const int per_seg = p.heads * p.tiles_max;
+    const int per_seg = p.heads * tiles_max;
     s = u / per_seg;
     const int rem = u - s * per_seg;
-    h = rem / p.tiles_max;
-    tile = rem - h * p.tiles_max;
+    h = rem / tiles_max;
+    tile = rem - h * tiles_max;
   }
   a = ld_table(p.cu, s);
   L = ld_table(p.cu, s + 1) - a;
@@ -172,14 +177,12 @@ template <int D, int CPT, int TAG>
 __device__ __forceinline__ void bwd_issue_tile(const __bf16* base, int r0, int L, int64_t rs,
                                                int row_bytes, char* dst, const int (&src)[CPT],
                                                int wave) {
-  using C = BwdTile<D>;
-  static_assert(CPT == C::CPT, "one source offset per chunk group");
   const int rows = (L - r0 < kBwdStage) ? (L - r0) : kBwdStage;
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)r0 * rs), 0, rows * row_bytes, kRsrcFlags);
-  dst += wave * C::CPT * 1024;
+  dst += wave * CPT * 1024;
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i)
+  for (int i = 0; i < CPT; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(dst + i * 1024), 16, src[i], 0, 0, 0);
 }
 
@@ -248,7 +251,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
 
   for (int u = slot; u < total; u += G) {
     int a, L, h, kt;
-    if (!bwd_item<kBwdRows>(p, u, sorted, s_order, s_prefix, T, a, L, h, kt)) continue;
+    if (!bwd_item<kBwdRows>(p, p.tiles_max, u, sorted, s_order, s_prefix, T, a, L, h, kt)) continue;
     const int64_t head_off = (int64_t)h * D;
     const int k0 = kt * kBwdRows + wave * 32;        // this wave's first key
     // stationary K^T and V^T fragments (B operands; lane n32 = key k0 + n32)
@@ -365,7 +368,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
     }
     __syncthreads();   // every wave has left the ring
     char* const ok = qring + wave * (32 * D * 2);
-    char* const ov = qring + (kBwdNW + wave) * (32 * D * 2);
+    char* const ov = qring + (kBwdNW + wave) * (32 * D * 2);   // 2 x kBwdNW blocks fit the ring
     stage_rows<D>(dkt, p.scale, ok, n32, g);
     stage_rows<D>(dvt, 1.0f, ov, n32, g);
     __syncthreads();
@@ -378,9 +381,9 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
 
 // ---- dQ
 template <int D>
-__global__ void __launch_bounds__(kWave * kBwdNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(kWave * kDqNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 pfa_bwd_dq_kernel(BwdParams p) {
-  using C = BwdTile<D>;
+  using C = BwdTile<D, kDqNW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   char* const kring = reinterpret_cast<char*>(smem);
   char* const vring = kring + kStages * C::TILE_BYTES;
@@ -391,9 +394,9 @@ pfa_bwd_dq_kernel(BwdParams p) {
   const int T = ld_table(p.cu, p.num_seqs);
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
-  const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
-                                                                   s_len, s_order, s_prefix, kSortMax)
-                           : p.num_seqs * p.heads * p.tiles_max;
+  const int total = sorted ? build_schedule<kDqRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
+                                                                  s_len, s_order, s_prefix, kSortMax)
+                           : p.num_seqs * p.heads * p.tiles_max_q;
   const int G = gridDim.x;
   const int bid = blockIdx.x;
   const int slot = (G % 8 == 0) ? (bid & 7) * (G >> 3) + (bid >> 3) : bid;
@@ -417,9 +420,9 @@ pfa_bwd_dq_kernel(BwdParams p) {
 
   for (int u = slot; u < total; u += G) {
     int a, L, h, qt;
-    if (!bwd_item<kBwdRows>(p, u, sorted, s_order, s_prefix, T, a, L, h, qt)) continue;
+    if (!bwd_item<kDqRows>(p, p.tiles_max_q, u, sorted, s_order, s_prefix, T, a, L, h, qt)) continue;
     const int64_t head_off = (int64_t)h * D;
-    const int q0 = qt * kBwdRows + wave * 32;
+    const int q0 = qt * kDqRows + wave * 32;
     const int row = q0 + n32;                        // this lane's query
     // stationary Q^T and dO^T fragments (B operands; lane n32 = query)
     bf16x8 qr[C::KSTEP], dr[C::KSTEP];
@@ -600,8 +603,11 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   const void* dqk = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_dq_kernel<64>)
                                    : reinterpret_cast<const void*>(&pfa_bwd_dq_kernel<128>);
   const size_t lds_dkdv = head_dim == 64 ? BwdTile<64>::LDS_DKDV : BwdTile<128>::LDS_DKDV;
-  const size_t lds_dq = head_dim == 64 ? BwdTile<64>::LDS_DQ : BwdTile<128>::LDS_DQ;
+  const size_t lds_dq = head_dim == 64 ? BwdTile<64, kDqNW>::LDS_DQ : BwdTile<128, kDqNW>::LDS_DQ;
   const int threads = kWave * kBwdNW;
+  const int threads_q = kWave * kDqNW;
+  const int64_t tiles_max_q = ((int64_t)max_seqlen + kDqRows - 1) / kDqRows;
+  const int64_t slots_q = (int64_t)num_seqs * heads * tiles_max_q;
   const int vi = head_dim == 64 ? 0 : 1;
   int occ_kv = g_bwd_occ[dev][vi][0].load(std::memory_order_relaxed);
   int occ_q = g_bwd_occ[dev][vi][1].load(std::memory_order_relaxed);
@@ -611,14 +617,14 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
       return PFA_ERR_DEVICE;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_kv, dkdv, threads, lds_dkdv) != hipSuccess ||
         occ_kv <= 0 ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_q, dqk, threads, lds_dq) != hipSuccess || occ_q <= 0)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_q, dqk, threads_q, lds_dq) != hipSuccess || occ_q <= 0)
       return PFA_ERR_DEVICE;
     g_bwd_occ[dev][vi][0].store(occ_kv, std::memory_order_relaxed);
     g_bwd_occ[dev][vi][1].store(occ_q, std::memory_order_relaxed);
   }
-  auto grid_for = [&](int occ) {
+  auto grid_for = [&](int occ, int64_t n_slots) {
     int64_t grid = (int64_t)cus * occ;
-    if (grid > slots) grid = slots;
+    if (grid > n_slots) grid = n_slots;
     if (grid >= 8) grid -= grid % 8;
     return (unsigned)grid;
   };
@@ -639,13 +645,14 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
   bp.num_seqs = num_seqs;
   bp.heads = heads;
   bp.tiles_max = (int)tiles_max;
+  bp.tiles_max_q = (int)tiles_max_q;
   bp.c = scale * kLog2e;
   bp.scale = scale;
   void* args[] = {&bp};
   // dQ first: it writes the row statistics the dK/dV pass reads
-  if (hipLaunchKernel(dqk, dim3(grid_for(occ_q)), dim3(threads), args, lds_dq, stream) != hipSuccess)
+  if (hipLaunchKernel(dqk, dim3(grid_for(occ_q, slots_q)), dim3(threads_q), args, lds_dq, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
-  if (hipLaunchKernel(dkdv, dim3(grid_for(occ_kv)), dim3(threads), args, lds_dkdv, stream) != hipSuccess)
+  if (hipLaunchKernel(dkdv, dim3(grid_for(occ_kv, slots)), dim3(threads), args, lds_dkdv, stream) != hipSuccess)
     return PFA_ERR_LAUNCH;
   return PFA_OK;
 }
