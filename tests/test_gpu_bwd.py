@@ -80,10 +80,24 @@ def test_random_ragged_packs(seed):
     _check(wl, _dout(wl, seed), f"ragged seed={seed} d={d} lengths={lengths}")
 
 
-@pytest.mark.parametrize("lengths", [[1, 2, 3], [64], [65], [127, 128, 129], [255, 256, 257]])
+@pytest.mark.parametrize("lengths", [[1, 2, 3], [64], [65], [127, 128, 129], [255, 256, 257],
+                                     [511, 512, 513]])
 def test_tile_boundaries(lengths):
+    # dK/dV items hold 128 keys, dQ items 256 queries, stages 64 rows
     wl = W.make(lengths, 2, 128, seed=7)
     _check(wl, _dout(wl, 7), f"boundaries {lengths}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_short_segments_slot_schedule(d):
+    """More segments than the on-device sort holds (512): both passes walk the slots
+    (segment, head, tile) in index order instead of the longest-first list.  Lengths 0..300
+    with empty segments among them, against the oracle."""
+    rng = np.random.default_rng(70 + d)
+    lengths = rng.integers(0, 301, size=600)
+    lengths[rng.choice(600, size=40, replace=False)] = 0
+    wl = W.make(lengths.tolist(), 2, d, seed=70 + d)
+    _check(wl, _dout(wl, 70 + d), f"600 segments d={d}")
 
 
 def test_c3_shape_on_two_heads():
