@@ -69,7 +69,10 @@ typedef enum pfa_status {
  * cu_seqlens  device pointer, int32 [num_seqs + 1]: segment s owns rows
  *             [cu_seqlens[s], cu_seqlens[s+1]).  The same table serves queries and keys.
  * num_seqs    number of segments (>= 1).  Zero-length segments are legal and do nothing.
- * max_seqlen  an upper bound on every segment length (>= 1); sizes the launch only.
+ * max_seqlen  an upper bound on every segment length (>= 1); sizes the launch and picks the
+ *             kernel: at most 256 (head_dim 128) or 128 (head_dim 64), each segment's K
+ *             and V are loaded into LDS whole (the resident kernel of pfa_varlen_fwd_qk),
+ *             above it they stream in 64-key stages.  Both give bitwise equal results.
  * heads       attention heads (>= 1); q, k and v all have this many (no grouped heads).
  * head_dim    64 or 128.
  * scale       factor on q.k, finite and > 0 (1/sqrt(head_dim) in the usual definition).
@@ -112,7 +115,8 @@ PFA_API int pfa_varlen_fwd(const void* q, const void* k, const void* v, const in
  * q, out        bf16 [Tq, heads, head_dim], Tq = cu_seqlens_q[num_seqs].
  * k, v          bf16 [Tk, heads, head_dim], Tk = cu_seqlens_k[num_seqs].
  * cu_seqlens_q, cu_seqlens_k   device int32 [num_seqs + 1]; passing the same pointer for
- *               both selects the self-attention kernel.
+ *               both selects the self-attention instantiation of the streaming kernel
+ *               (when max_seqlen_k is above the resident bound below).
  * max_seqlen_q  bound on every query segment length (>= 1); sizes the launch.
  * max_seqlen_k  bound on every key segment length (>= 1).  At most 256 (head_dim 128) or
  *               128 (head_dim 64) selects a kernel that holds each (segment, head)'s K and V

@@ -1330,10 +1330,12 @@ PFA_API int pfa_varlen_fwd_qk(const void* q, const void* k, const void* v, const
   prm.num_seqs = num_seqs;
   prm.heads = heads;
   prm.c = scale * kLog2e;
-  // separate tables whose key segments all fit in LDS: the resident-K/V kernel
+  // key segments that all fit in LDS: the resident-K/V kernel, for self-attention too (a
+  // short segment's tiles then load its K/V in one go; with one tile per segment there is
+  // nothing to reuse, but the tile's stages no longer wait on a streamed ring)
   const int resident_max = head_dim == 64 ? resident_keys<64>() : resident_keys<128>();
-  const int mode = cu_seqlens_k == cu_seqlens_q ? kModeSelf
-                 : max_seqlen_k <= resident_max  ? kModeResident
+  const int mode = max_seqlen_k <= resident_max        ? kModeResident
+                 : cu_seqlens_k == cu_seqlens_q ? kModeSelf
                                                  : kModeCross;
   return launch_fwd(prm, mode, max_seqlen_q, head_dim, stream);
 }
