@@ -714,6 +714,12 @@ pfa_fwd_kernel(Params p) {
     total = p.num_seqs * p.heads * p.qt_max;
   }
 
+  // Items of a segment: head-major, so consecutive items (one XCD's run in a round) share
+  // a (segment, head) and its K/V.  Block-sparse lists differ from tile to tile (a band
+  // lists fewer key blocks at a segment's edges), and with head-major order a workgroup
+  // would meet the same tile index in every round whenever the tiles per segment divide
+  // the grid; there the items are tile-major (heads fastest) instead.
+  constexpr bool kTileMajor = mode_sparse(MODE);
   // XCD-aware placement: workgroup b runs on XCD b % 8; give each XCD a contiguous run
   // of the (longest-first) item list in every round.
   const int G = gridDim.x;
@@ -733,14 +739,24 @@ pfa_fwd_kernel(Params p) {
       s = __builtin_amdgcn_readfirstlane(s_order[lo]);
       const int ntiles = (ld_table(p.cu_q, s + 1) - ld_table(p.cu_q, s) + C::BM - 1) / C::BM;
       const int local = u - __builtin_amdgcn_readfirstlane(s_prefix[lo]);
-      h = local / ntiles;
-      qt = local - h * ntiles;
+      if constexpr (kTileMajor) {
+        qt = local / p.heads;
+        h = local - qt * p.heads;
+      } else {
+        h = local / ntiles;
+        qt = local - h * ntiles;
+      }
     } else {
       const int per_seg = p.heads * p.qt_max;
       s = u / per_seg;
       const int rem = u - s * per_seg;
-      h = rem / p.qt_max;
-      qt = rem - h * p.qt_max;
+      if constexpr (kTileMajor) {
+        qt = rem / p.heads;
+        h = rem - qt * p.heads;
+      } else {
+        h = rem / p.qt_max;
+        qt = rem - h * p.qt_max;
+      }
     }
     const int qa = ld_table(p.cu_q, s);
     int Lq = ld_table(p.cu_q, s + 1) - qa;
