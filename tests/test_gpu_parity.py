@@ -250,3 +250,22 @@ def test_tensors_beyond_two_giga_elements():
         G.assert_parity(G.compare(ob[rows], ls[:, rows], o_ref, l_ref), f"segment {s} (block {c})")
     del big, out, lse
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d,bound", [(128, 256), (64, 128)])
+def test_short_segments_resident_kernel_equals_streaming(d, bound):
+    """max_seqlen only selects the kernel: at most the resident bound (256 keys at d = 128,
+    128 at d = 64) each segment's K/V are loaded into LDS whole, one above it they stream in
+    64-key stages.  Both must give the same bits, and match the oracle."""
+    import dataclasses
+    rng = np.random.default_rng(90 + d)
+    lengths = rng.integers(0, bound + 1, size=300).tolist()
+    lengths[:4] = [bound, 1, 0, bound - 1]
+    wl = W.make(lengths, 3, d, seed=90 + d, name="short")
+    assert wl.max_seqlen <= bound
+    dev = G.upload(wl)
+    o_res, l_res = G.run(wl, f"resident (max_seqlen {wl.max_seqlen}) d={d}", dev=dev)
+    o_str, l_str = G.run(dataclasses.replace(wl, max_seqlen=bound + 1), f"streaming (max_seqlen {bound + 1}) d={d}", dev=dev)
+    assert np.array_equal(o_res, o_str) and np.array_equal(l_res.view(np.uint32), l_str.view(np.uint32))
+    o_ref, l_ref = oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale)
+    G.assert_parity(G.compare(o_res, l_res, o_ref, l_ref), f"short segments d={d}")
