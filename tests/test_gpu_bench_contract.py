@@ -54,3 +54,19 @@ def test_bench_line_fields(extra):
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 2e-3
     assert roof["traffic"] is None or roof["traffic"] > 0
     say(f"   value {rec['value']} {rec['unit']}, roofline {roof['achieved']} / {roof['peak']} {roof['unit']}")
+
+
+def test_default_warmup_is_resolved_from_the_step_time():
+    """Without --warmup the warm-up count is resolved to at least 0.15 s of GPU work (at
+    least 50 launches), so the timed steps run at the settled clock; the line reports it."""
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "2", "--no-cpu-baseline",
+           "--config", "C1"]
+    say("[gpu] bench --config C1, default warm-up")
+    res = subprocess.run(cmd, capture_output=True, text=True, timeout=240, cwd=ROOT)
+    assert res.returncode == 0, res.stdout[-2000:] + res.stderr[-2000:]
+    rec = json.loads([ln for ln in res.stdout.splitlines() if ln.startswith("{")][-1])
+    kernel_ms = rec["roofline"]["kernel_ms"]
+    assert rec["warmup"] >= 50
+    # a C1 launch takes ~12 us, so 0.15 s of work is thousands of launches
+    assert rec["warmup"] * kernel_ms >= 0.1 * 150.0, (rec["warmup"], kernel_ms)
+    say(f"   warm-up {rec['warmup']} launches of {kernel_ms:.4f} ms")
