@@ -87,6 +87,25 @@ def test_every_block_listed_equals_the_dense_kernel_bitwise():
     np.testing.assert_array_equal(lse, lse2.cpu().numpy())
 
 
+def test_beyond_the_sort_capacity_every_block_listed_equals_dense_bitwise():
+    """4,200 segments, more than the on-device sort holds (4,096): both kernels walk the
+    slots (segment, head, tile) in index order, the block-sparse one tile-major.  With every
+    block listed the results equal the dense kernel's bit for bit."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd
+    rng = np.random.default_rng(317)
+    lengths = [int(x) for x in rng.integers(0, 301, size=4200)]
+    lengths[0] = 300                                   # the streaming dense kernel (> 256 keys)
+    wl = W.make(lengths, 2, 128, seed=317, name="4200 segments")
+    full = [[[list(range(-(-L // 64))) for _ in range(-(-L // 256))] for L in wl.lengths]]
+    ob, lse = _run(wl, full, "4200 segments, every block listed")
+    cu = torch.from_numpy(wl.cu_seqlens).to("cuda")
+    out2, lse2 = pfa_varlen_fwd(to_dev(wl.q), to_dev(wl.k), to_dev(wl.v), cu, wl.max_seqlen, wl.scale)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ob, from_dev_bf16(out2))
+    np.testing.assert_array_equal(lse, lse2.cpu().numpy())
+
+
 def test_list_order_does_not_change_the_retained_set():
     wl, rng = _pack(312, 128)
     lay = W.random_layout(rng, wl.lengths, 1, density=0.6)
