@@ -26,14 +26,16 @@ namespace {
 // offsets for each 16-row step and 8-row half, since the swizzle does not keep a constant
 // pattern 8 rows apart.
 // ---------------------------------------------------------------------------------
-// Waves per workgroup.  dK/dV: four, one per SIMD; it holds two accumulators and the
-// stationary K and V fragments (450 registers at d = 128), so one workgroup fills a CU
-// (at d = 64 it fits 256 registers and two workgroups share a CU).  dQ: eight, two per
+// Waves per workgroup.  dK/dV at d = 128: four, one per SIMD; it holds two accumulators
+// and the stationary K and V fragments (450 registers), so one workgroup fills a CU.  At
+// d = 64 it fits 256 registers: eight waves, two per SIMD, 256 keys per item.  dQ: eight, two per
 // SIMD; it loads its two operand sets one after the other and fits 256 registers (its few
 // spills are per-item offsets, reloaded outside the stage loop), and one K/V stage load
 // feeds 256 queries.
 constexpr int kBwdNW = 4;
-constexpr int kBwdRows = kBwdNW * 32;      // keys per dK/dV work item
+constexpr int kBwdRows = kBwdNW * 32;      // keys per dK/dV work item at d = 128 (bounds slot counts)
+template <int D>
+constexpr int kDkdvNW = D == 64 ? 8 : kBwdNW;   // dK/dV waves per workgroup
 constexpr int kDqNW = 8;
 constexpr int kDqRows = kDqNW * 32;        // queries per dQ work item
 constexpr int kBwdStage = 64;              // rows per streamed stage
@@ -68,9 +70,12 @@ struct BwdTile {
   static constexpr int DT = D / 32;
   static constexpr int KSTEP = D / 16;
   static constexpr int ROWF_BYTES = kBwdStage * 4;           // one 64-row fp32 vector
-  // dK/dV: [Q ring][dO ring][row-vector ring: 2 x (neg_lse2, delta)] + schedule
-  static constexpr size_t LDS_DKDV = (size_t)kStages * 2 * TILE_BYTES + kStages * 2 * ROWF_BYTES +
-                                     sizeof(int) * (2 * kSortMax + 8);
+  // dK/dV: [Q ring][dO ring][row-vector ring: 2 x (neg_lse2, delta)], which the epilogue
+  // reuses for the staged dK and dV blocks (one each per wave), then the schedule
+  static constexpr int DKDV_RING = (kStages * 2 * TILE_BYTES + kStages * 2 * ROWF_BYTES > 2 * NW * 32 * D * 2)
+                                       ? kStages * 2 * TILE_BYTES + kStages * 2 * ROWF_BYTES
+                                       : 2 * NW * 32 * D * 2;
+  static constexpr size_t LDS_DKDV = (size_t)DKDV_RING + sizeof(int) * (2 * kSortMax + 8);
   // dQ: [K ring][V ring] + schedule
   static constexpr size_t LDS_DQ = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * (2 * kSortMax + 8);
   static_assert(CPT * THREADS == kBwdStage * CPR, "stage must split evenly");
@@ -210,23 +215,25 @@ template <int D>
 constexpr int kDkdvWavesPerEu = D == 64 ? 2 : 1;
 
 template <int D>
-__global__ void __launch_bounds__(kWave * kBwdNW)
+__global__ void __launch_bounds__(kWave * kDkdvNW<D>)
 __attribute__((amdgpu_waves_per_eu(kDkdvWavesPerEu<D>, kDkdvWavesPerEu<D>)))
 pfa_bwd_dkdv_kernel(BwdParams p) {
-  using C = BwdTile<D>;
+  constexpr int NW = kDkdvNW<D>;
+  constexpr int ROWS = NW * 32;                                   // keys per work item
+  using C = BwdTile<D, NW>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   char* const qring = reinterpret_cast<char*>(smem);
   char* const dring = qring + kStages * C::TILE_BYTES;
   char* const fring = dring + kStages * C::TILE_BYTES;            // [slot][neg_lse2 | delta]
-  int* s_order = reinterpret_cast<int*>(fring + kStages * 2 * C::ROWF_BYTES);
+  int* s_order = reinterpret_cast<int*>(qring + C::DKDV_RING);
   int* s_prefix = s_order + kSortMax;
   int* s_len = reinterpret_cast<int*>(qring);
 
   const int T = ld_table(p.cu, p.num_seqs);
   if (T > p.ws_rows) return;   // uniform across the workgroup, before any barrier
   const bool sorted = p.num_seqs <= kSortMax;
-  const int total = sorted ? build_schedule<kBwdRows, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
-                                                                   s_len, s_order, s_prefix, kSortMax)
+  const int total = sorted ? build_schedule<ROWS, C::THREADS>(p.cu, p.cu, p.num_seqs, p.heads,
+                                                               s_len, s_order, s_prefix, kSortMax)
                            : p.num_seqs * p.heads * p.tiles_max;
   const int G = gridDim.x;
   const int bid = blockIdx.x;
@@ -251,9 +258,9 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
 
   for (int u = slot; u < total; u += G) {
     int a, L, h, kt;
-    if (!bwd_item<kBwdRows>(p, p.tiles_max, u, sorted, s_order, s_prefix, T, a, L, h, kt)) continue;
+    if (!bwd_item<ROWS>(p, p.tiles_max, u, sorted, s_order, s_prefix, T, a, L, h, kt)) continue;
     const int64_t head_off = (int64_t)h * D;
-    const int k0 = kt * kBwdRows + wave * 32;        // this wave's first key
+    const int k0 = kt * ROWS + wave * 32;            // this wave's first key
     // stationary K^T and V^T fragments (B operands; lane n32 = key k0 + n32)
     bf16x8 kr[C::KSTEP], vr[C::KSTEP];
     {
@@ -368,7 +375,7 @@ pfa_bwd_dkdv_kernel(BwdParams p) {
     }
     __syncthreads();   // every wave has left the ring
     char* const ok = qring + wave * (32 * D * 2);
-    char* const ov = qring + (kBwdNW + wave) * (32 * D * 2);   // 2 x kBwdNW blocks fit the ring
+    char* const ov = qring + (NW + wave) * (32 * D * 2);       // 2 x NW blocks fit DKDV_RING
     stage_rows<D>(dkt, p.scale, ok, n32, g);
     stage_rows<D>(dvt, 1.0f, ov, n32, g);
     __syncthreads();
@@ -593,7 +600,8 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
                const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int heads,
                int head_dim, float scale, void* dq, void* dk, void* dv, float* ws, int ws_rows,
                hipStream_t stream) {
-  const int64_t tiles_max = ((int64_t)max_seqlen + kBwdRows - 1) / kBwdRows;
+  const int rows_kv = 32 * (head_dim == 64 ? kDkdvNW<64> : kDkdvNW<128>);
+  const int64_t tiles_max = ((int64_t)max_seqlen + rows_kv - 1) / rows_kv;
   const int64_t slots = (int64_t)num_seqs * heads * tiles_max;
   int dev = 0, cus = 0;
   const int rc = device_cus(&dev, &cus);
@@ -602,9 +610,9 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* out, con
                                     : reinterpret_cast<const void*>(&pfa_bwd_dkdv_kernel<128>);
   const void* dqk = head_dim == 64 ? reinterpret_cast<const void*>(&pfa_bwd_dq_kernel<64>)
                                    : reinterpret_cast<const void*>(&pfa_bwd_dq_kernel<128>);
-  const size_t lds_dkdv = head_dim == 64 ? BwdTile<64>::LDS_DKDV : BwdTile<128>::LDS_DKDV;
+  const size_t lds_dkdv = head_dim == 64 ? BwdTile<64, kDkdvNW<64>>::LDS_DKDV : BwdTile<128, kDkdvNW<128>>::LDS_DKDV;
   const size_t lds_dq = head_dim == 64 ? BwdTile<64, kDqNW>::LDS_DQ : BwdTile<128, kDqNW>::LDS_DQ;
-  const int threads = kWave * kBwdNW;
+  const int threads = kWave * (head_dim == 64 ? kDkdvNW<64> : kDkdvNW<128>);
   const int threads_q = kWave * kDqNW;
   const int64_t tiles_max_q = ((int64_t)max_seqlen + kDqRows - 1) / kDqRows;
   const int64_t slots_q = (int64_t)num_seqs * heads * tiles_max_q;
