@@ -80,12 +80,13 @@ def test_random_ragged_packs(seed):
     _check(wl, _dout(wl, seed), f"ragged seed={seed} d={d} lengths={lengths}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("lengths", [[1, 2, 3], [64], [65], [127, 128, 129], [255, 256, 257],
                                      [511, 512, 513]])
-def test_tile_boundaries(lengths):
-    # dK/dV items hold 128 keys, dQ items 256 queries, stages 64 rows
-    wl = W.make(lengths, 2, 128, seed=7)
-    _check(wl, _dout(wl, 7), f"boundaries {lengths}")
+def test_tile_boundaries(lengths, d):
+    # dK/dV items hold 128 keys (d = 128) or 256 (d = 64), dQ items 256 queries, stages 64 rows
+    wl = W.make(lengths, 2, d, seed=7)
+    _check(wl, _dout(wl, 7), f"boundaries {lengths} d={d}")
 
 
 @pytest.mark.parametrize("d", [64, 128])
