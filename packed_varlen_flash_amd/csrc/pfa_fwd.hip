@@ -107,7 +107,10 @@ struct Tile {
   static constexpr int SCHED_INTS = 2 * kSortMax + 8;
   static constexpr int CPR8 = D / 16;               // 16-byte chunks per e4m3 V row
   static constexpr int CPT8 = SK * CPR8 / THREADS;  // e4m3 V chunks per thread per stage
-  static constexpr size_t LDS_BYTES = (size_t)kStages * 2 * TILE_BYTES + sizeof(int) * SCHED_INTS;
+  // the K/V ring, which the epilogue reuses to stage each wave's output block
+  static constexpr int RING_BYTES = (kStages * 2 * TILE_BYTES > NW * QB * 32 * D * 2)
+                                        ? kStages * 2 * TILE_BYTES : NW * QB * 32 * D * 2;
+  static constexpr size_t LDS_BYTES = (size_t)RING_BYTES + sizeof(int) * SCHED_INTS;
   static_assert(CPT * THREADS == SK * CPR, "stage must split evenly");
   static_assert(SK % kHalf == 0, "stages hold whole 64-key halves");
   static_assert(sizeof(int) * kSortMax <= (size_t)kStages * TILE_BYTES, "len scratch fits");
@@ -647,7 +650,7 @@ __device__ __forceinline__ void process_tile(const Params& p, __bf16* ks, __bf16
   // ring in the swizzled K layout, then reads it back as whole 16-byte chunks of
   // consecutive rows, so 16 lanes store 256 contiguous bytes instead of every store
   // instruction touching 16-byte pieces of 32 different rows.
-  static_assert(NW * QB * 32 * D * 2 <= 2 * kStages * C::TILE_BYTES, "O staging fits the ring");
+  static_assert(NW * QB * 32 * D * 2 <= C::RING_BYTES, "O staging fits the ring");
   char* const ost = kring + wave * (QB * 32 * D * 2);
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
@@ -698,7 +701,7 @@ pfa_fwd_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __bf16* ks = reinterpret_cast<__bf16*>(smem);
   __bf16* vs = reinterpret_cast<__bf16*>(smem + kStages * C::TILE_BYTES);
-  int* s_order = reinterpret_cast<int*>(smem + 2 * kStages * C::TILE_BYTES);
+  int* s_order = reinterpret_cast<int*>(smem + C::RING_BYTES);
   int* s_prefix = s_order + p.sort_cap;
   int* s_blk = s_order + 2 * p.sort_cap + 8;   // block-sparse variant only (its LDS is larger)
   int* s_len = reinterpret_cast<int*>(ks);     // scratch, dead before the first K tile lands
@@ -1174,13 +1177,16 @@ Variant make_variant() {
                  C::THREADS, C::LDS_BYTES + (mode_sparse(MODE) ? kSparseLdsBytes : 0)};
 }
 
-// head_dim 64, 128 x (the six kernel modes, the resident-K/V cross kernel)
+// head_dim 64, 128 x (the six kernel modes, the resident-K/V cross kernel), plus the
+// eight-wave d = 64 variants of the self, cross and fused-QKV modes
 constexpr int kModeResident = 6;
-constexpr int kVariants = 14;
+constexpr int kVariants = 17;
 constexpr int kSortClasses = 4;   // schedule capacities 512, 1024, 2048, 4096
 std::atomic<int> g_occ[kMaxDevices][kVariants][kSortClasses];
 
-int variant_index(int head_dim, int mode) { return (head_dim == 64 ? 0 : 1) + 2 * mode; }
+int variant_index(int head_dim, int mode, bool wide) {
+  return wide ? 14 + (mode == kModeCross ? 1 : mode == kModeQkv ? 2 : 0) : (head_dim == 64 ? 0 : 1) + 2 * mode;
+}
 
 template <int D, int QB, int NW, int WPE>
 Variant make_resident_variant() {
@@ -1214,10 +1220,26 @@ Variant make_resident_variant() {
 #define PFA_D128_SK 64
 #endif
 
-template <int MODE>
+template <int MODE, int NW64 = PFA_D64_NW>
 Variant variant_of(int head_dim) {
-  if (head_dim == 64) return make_variant<64, PFA_D64_QB, PFA_D64_NW, PFA_D64_SK, PFA_D64_WPE, MODE>();
+  if (head_dim == 64) return make_variant<64, PFA_D64_QB, NW64, PFA_D64_SK, PFA_D64_WPE, MODE>();
   return make_variant<128, PFA_D128_QB, PFA_D128_NW, PFA_D128_SK, PFA_D128_WPE, MODE>();
+}
+
+// d = 64 with query segments of 512 rows or more: eight waves (512-query tiles), so each
+// K/V stage load feeds twice the queries.  Shorter segments keep four waves, which would
+// otherwise idle half of a 512-query tile.  The block-sparse modes keep the 256-query
+// tile their layouts are made of, the FP8 modes the four-wave split of their V loads.
+constexpr int kD64WideNW = 8;
+constexpr int kWideMinQ = 512;
+bool use_wide64(int head_dim, int mode, int max_seqlen_q) {
+  return head_dim == 64 && max_seqlen_q >= kWideMinQ &&
+         (mode == kModeSelf || mode == kModeCross || mode == kModeQkv);
+}
+Variant wide64_for(int mode) {
+  return mode == kModeCross ? variant_of<kModeCross, kD64WideNW>(64)
+       : mode == kModeQkv   ? variant_of<kModeQkv, kD64WideNW>(64)
+                            : variant_of<kModeSelf, kD64WideNW>(64);
 }
 
 Variant variant_for(int head_dim, int mode) {
@@ -1235,7 +1257,8 @@ Variant variant_for(int head_dim, int mode) {
 // Size the persistent grid of one forward variant and launch it.  prm carries every
 // field but qt_max; the caller has checked the arguments.
 int launch_fwd(Params prm, int mode, int max_seqlen_q, int head_dim, hipStream_t stream) {
-  const Variant var = variant_for(head_dim, mode);
+  const bool wide = use_wide64(head_dim, mode, max_seqlen_q);
+  const Variant var = wide ? wide64_for(mode) : variant_for(head_dim, mode);
   const int64_t qt_max = ((int64_t)max_seqlen_q + var.bm - 1) / var.bm;
   const int64_t slots = (int64_t)prm.num_seqs * prm.heads * qt_max;
   if (slots > INT32_MAX) return PFA_ERR_SIZE;
@@ -1253,7 +1276,7 @@ int launch_fwd(Params prm, int mode, int max_seqlen_q, int head_dim, hipStream_t
     }
   const size_t lds = var.lds + sizeof(int) * 2 * (size_t)(cap - kSortMax);
   const size_t lds_max = mode == kModeResident ? var.lds : var.lds + sizeof(int) * 2 * (size_t)(kSortCapMax - kSortMax);
-  const int vi = variant_index(head_dim, mode);
+  const int vi = variant_index(head_dim, mode, wide);
   int occ = g_occ[dev][vi][cls].load(std::memory_order_relaxed);
   if (occ <= 0) {
     if (hipFuncSetAttribute(var.fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max) != hipSuccess)
