@@ -10,7 +10,7 @@
 // the final output (and here the log-sum-exp) back to HBM.
 //
 // gfx950 mapping (d = 128: one workgroup = 8 wave64s on one CU, two waves per SIMD;
-// d = 64: 4 wave64s):
+// d = 64: 4 wave64s, or 8 for query segments of 512 rows or more):
 //   * work unit = (segment, head, BM-row query tile); a tile never spans two segments.
 //     Tiles are listed longest segment first and handed out round-robin by a persistent
 //     grid; each XCD receives contiguous runs of the list so the query tiles that share
