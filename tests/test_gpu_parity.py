@@ -269,3 +269,35 @@ def test_short_segments_resident_kernel_equals_streaming(d, bound):
     assert np.array_equal(o_res, o_str) and np.array_equal(l_res.view(np.uint32), l_str.view(np.uint32))
     o_ref, l_ref = oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale)
     G.assert_parity(G.compare(o_res, l_res, o_ref, l_ref), f"short segments d={d}")
+
+
+def test_d64_four_and_eight_wave_tiles_agree_bitwise():
+    """At d = 64 a query bound of 512 rows or more selects 512-query tiles of eight waves,
+    below it 256-query tiles of four.  max_seqlen is only a bound, so the same pack (every
+    segment under 512 rows) run with 511 and with 512 must give the same bits, for the
+    self-attention, separate-table and fused-QKV entry points."""
+    import torch
+    from packed_varlen_flash_amd import pfa_varlen_fwd, pfa_varlen_fwd_qk, pfa_varlen_fwd_qkv
+    rng = np.random.default_rng(95)
+    lengths = rng.integers(0, 512, size=40).tolist()
+    lengths[:3] = [511, 257, 1]
+    wl = W.make(lengths, 3, 64, seed=95, name="d64 tiles")
+    q, k, v, cu = G.upload(wl)
+    cu_k = cu.clone()       # a second table: the cross mode (a key bound of 511 or 512 is
+                            # above the resident kernel's 128 keys, so it streams K/V)
+    qkv = torch.stack([q, k, v], dim=1).contiguous()   # [T, 3, H, d]
+    res = {}
+    for bound in (511, 512):
+        o1, l1 = pfa_varlen_fwd(q, k, v, cu, bound, wl.scale)
+        o2, l2 = pfa_varlen_fwd_qk(q, k, v, cu, cu_k, bound, bound, wl.scale)
+        o3, l3, _ = pfa_varlen_fwd_qkv(qkv, cu, bound, wl.scale)
+        torch.cuda.synchronize()
+        res[bound] = [t.view(torch.int16 if t.dtype == torch.bfloat16 else torch.int32).cpu()
+                      for t in (o1, l1, o2, l2, o3, l3)]
+        G.say(f"[gpu] d=64 self / cross / fused-QKV with max_seqlen {bound}")
+    for a, b in zip(res[511], res[512]):
+        assert torch.equal(a, b)
+    assert torch.equal(res[511][0], res[511][2]) and torch.equal(res[511][0], res[511][4])
+    o_ref, l_ref = oracle.varlen_fwd(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.scale)
+    out = res[512][0].numpy().view(np.uint16)
+    G.assert_parity(G.compare(out, res[512][1].numpy().view(np.float32), o_ref, l_ref), "d=64 eight-wave tiles")
