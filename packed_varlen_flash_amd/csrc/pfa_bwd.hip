@@ -55,7 +55,7 @@ struct BwdParams {
   __bf16* dv;
   int num_seqs;
   int heads;
-  int tiles_max;          // ceil(max_seqlen / kBwdRows): dK/dV slots per (segment, head), unsorted mode
+  int tiles_max;          // ceil(max_seqlen / dK/dV keys per item): slots per (segment, head), unsorted mode
   int tiles_max_q;        // ceil(max_seqlen / kDqRows): the same for dQ
   float c;                // scale * log2(e)
   float scale;
